@@ -1,0 +1,141 @@
+"""Seeded synthetic attention inputs shaped like the self- and cross-attention of Wan-style video DiTs.
+
+This module draws random numbers and nothing else: it holds none of the attention or quantization
+arithmetic.  Both the GPU path (tests, benchmark) and the CPU oracle are fed from it, so they see the
+identical bf16 bit patterns.
+
+Every (batch, head) slice is drawn from its own PCG64 stream seeded with ``SeedSequence([seed, b, h])``,
+so a single head can be regenerated on its own (the oracle only ever needs a few heads of a large
+workload).  Per slice, the draw order is: Q, K, V (``standard_normal`` float32, ``[N, d]``), then the
+per-channel K offsets, then the outlier-channel picks, then the zero-block picks.  K is formed in fp32
+(base + offset, outlier channels multiplied by 10), then every tensor is rounded to bf16 (round to
+nearest even, via torch's CPU cast), then zeroed channels / blocks are set to exact zero.
+
+Sequence lengths follow Wan's latent grids: 21 x 30 x 52 = 32 760 tokens (480p, 81 frames) and
+21 x 45 x 80 = 75 600 tokens (720p); cross-attention keys are 512 text + 257 image tokens = 769.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Tuple
+
+import numpy as np
+import torch
+
+# Distribution recipes (K offset per channel; extras):
+#   "tiny"     : Q, V ~ N(0,1); K ~ N(0,1) + U(-4, 4) per channel; channel 0 of K is all zeros.
+#   "outlier"  : Q, K, V ~ N(0,1); K + N(0, 3^2) per channel; 4 distinct channels of K scaled x10.
+#   "zeroblk"  : Q, K, V ~ N(0,1); K + N(0, 3^2) per channel; 1 % of the 64-token K blocks all zero.
+#   "plain"    : Q, K, V ~ N(0,1).
+DISTS = ("tiny", "outlier", "zeroblk", "plain")
+
+MODE_NAMES = {0: "bf16", 1: "i8-qk+bf16-pv", 2: "i8-qk+fp8-pv"}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nkv: int
+    d: int
+    blk_q: int
+    blk_k: int
+    dist: str
+    seed: int
+    modes: Tuple[int, ...]
+
+    @property
+    def ops(self) -> float:
+        """Effective attention operations per call: 4 * Nq * Nkv * d * H * B (QK^T and PV, 2 ops/MAC)."""
+        return 4.0 * self.Nq * self.Nkv * self.d * self.H * self.B
+
+    @property
+    def sm_scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.d))
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("tiny", 1, 2, 256, 256, 64, 64, 64, "tiny", 0, (1,)),
+        Workload("wan1.3b-480p", 1, 12, 32760, 32760, 128, 128, 64, "outlier", 1, (1,)),
+        Workload("wan14b-480p", 1, 40, 32760, 32760, 128, 128, 64, "outlier", 2, (0, 1, 2)),
+        Workload("wan14b-720p", 1, 40, 75600, 75600, 128, 128, 64, "zeroblk", 3, (2,)),
+        # one self-attention layer of the layer-selective pass (layer l uses seed 1000 + l) ...
+        Workload("layersel-720p-self", 1, 40, 75600, 75600, 128, 128, 64, "plain", 1000, (0, 2)),
+        # ... and its cross-attention call (layer l uses seed 2000 + l): 512 text + 257 image keys
+        Workload("layersel-720p-cross", 1, 40, 75600, 769, 128, 128, 64, "plain", 2000, (0, 1, 2)),
+    ]
+}
+
+LAYERSEL_LAYERS = 40
+LAYERSEL_BF16_LAYERS = 8
+LAYERSEL_MASK_SEED = 999
+
+
+def layer_modes(n_layers: int = LAYERSEL_LAYERS, n_bf16: int = LAYERSEL_BF16_LAYERS,
+                seed: int = LAYERSEL_MASK_SEED) -> list:
+    """Fixed seeded per-layer mode mask: ``n_bf16`` layers stay in bf16 (mode 0), the rest INT8+FP8 (2)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    keep = set(int(i) for i in rng.choice(n_layers, size=n_bf16, replace=False))
+    return [0 if i in keep else 2 for i in range(n_layers)]
+
+
+def _to_bf16(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(x).to(torch.bfloat16)
+
+
+def head_inputs(w: Workload, b: int, h: int, seed: int | None = None):
+    """Q [Nq, d], K [Nkv, d], V [Nkv, d] as CPU bf16 tensors for one (batch, head) slice."""
+    s = w.seed if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([s, b, h])))
+    d = w.d
+    q = rng.standard_normal((w.Nq, d), dtype=np.float32)
+    k = rng.standard_normal((w.Nkv, d), dtype=np.float32)
+    v = rng.standard_normal((w.Nkv, d), dtype=np.float32)
+    zero_channels = []
+    zero_blocks = []
+    if w.dist == "tiny":
+        k += rng.uniform(-4.0, 4.0, size=(1, d)).astype(np.float32)
+        zero_channels = [0]
+    elif w.dist in ("outlier", "zeroblk"):
+        k += (3.0 * rng.standard_normal((1, d))).astype(np.float32)
+        if w.dist == "outlier":
+            ch = rng.choice(d, size=4, replace=False)
+            k[:, ch] *= np.float32(10.0)
+        else:
+            nblk = (w.Nkv + 63) // 64
+            nzero = int(round(0.01 * nblk))
+            zero_blocks = [int(i) for i in rng.choice(nblk, size=nzero, replace=False)]
+    elif w.dist != "plain":
+        raise ValueError(f"unknown distribution {w.dist!r}")
+    qt, kt, vt = _to_bf16(q), _to_bf16(k), _to_bf16(v)
+    for c in zero_channels:
+        kt[:, c] = 0
+    for blk in zero_blocks:
+        kt[blk * 64:(blk + 1) * 64, :] = 0
+    return qt, kt, vt
+
+
+def full_inputs(w: Workload, seed: int | None = None):
+    """Q [B, H, Nq, d], K/V [B, H, Nkv, d] CPU bf16 tensors, head by head from ``head_inputs``."""
+    q = torch.empty((w.B, w.H, w.Nq, w.d), dtype=torch.bfloat16)
+    k = torch.empty((w.B, w.H, w.Nkv, w.d), dtype=torch.bfloat16)
+    v = torch.empty((w.B, w.H, w.Nkv, w.d), dtype=torch.bfloat16)
+    for b in range(w.B):
+        for h in range(w.H):
+            q[b, h], k[b, h], v[b, h] = head_inputs(w, b, h, seed)
+    return q, k, v
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """Raw 16-bit patterns of a CPU bf16 tensor as a numpy uint16 array (no copy of the values' meaning)."""
+    assert t.dtype == torch.bfloat16
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def scaled(w: Workload, **changes) -> Workload:
+    """The same recipe at other sizes (for tests that need a smaller instance of a workload)."""
+    return dataclasses.replace(w, **changes)

@@ -1,0 +1,258 @@
+"""Pins for the oracle's attention: the fp64 reference R (exact softmax(c*q*K^T)*V, the scaled-dot-product
+attention operator named in the TMAP I2V write-up's FLOP table, section "Attention 性能优化 / 背景") and the
+tile-faithful emulation E of the quantized modes (online softmax over key tiles, never materialising the
+score matrix; tutorial "视频生成推理加速实战:从基线到27倍", step 3, item "算子融合与高效注意力").
+
+Pins: closed forms (one key, uniform attention, two keys = logistic), invariants (rows of P sum to one,
+shift invariance), an exactly representable multi-tile case whose result is known as a rational number,
+agreement of the bf16 mode with R within the bf16 rounding bound, independence from the tile width, and
+the zero-guard special cases (all-zero K' block or channel -> finite, uniform attention).
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from quantized_attention_05_amd import workloads as wl
+
+LOG2E_F32 = np.float32(1.4426950408889634)
+
+
+def to_bf(x) -> np.ndarray:
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def exact_bf(x) -> np.ndarray:
+    x = np.asarray(x, dtype=np.float32)
+    h = to_bf(x)
+    assert np.array_equal(f32(h), x)
+    return h
+
+
+def f32(h):
+    return (np.asarray(h).astype(np.uint32) << 16).view(np.float32)
+
+
+def bf_round(x64: np.ndarray) -> np.ndarray:
+    """fp64 -> fp32 -> bf16 (round to nearest even each time), as 16-bit patterns."""
+    return to_bf(np.asarray(x64, dtype=np.float64).astype(np.float32))
+
+
+def unit_scale_sm():
+    """An sm_scale c with fp32(c * log2 e) == 1 exactly, so the logits in base 2 equal the integer scores."""
+    c = np.float32(math.log(2.0))
+    for _ in range(64):
+        if np.float32(c * LOG2E_F32) == np.float32(1.0):
+            return float(c)
+        c = np.nextafter(c, np.float32(1.0) if np.float32(c * LOG2E_F32) < 1 else np.float32(0.0))
+    raise AssertionError("no unit scale found")
+
+
+def rand_bf(shape, seed, scale=1.0):
+    rng = np.random.default_rng(seed)
+    return to_bf(rng.standard_normal(shape) * scale)
+
+
+# -------------------------------------------------------------------------------------------- R closed forms
+def test_ref_one_key_is_v0(orc):
+    q, k, v = rand_bf((5, 32), 1), rand_bf((1, 32), 2), rand_bf((1, 32), 3)
+    o = orc.attn_ref_fp64(q, k, v, range(5), 0.2)
+    assert np.array_equal(o, np.repeat(f32(v).astype(np.float64), 5, axis=0))
+
+
+def test_ref_zero_query_is_mean_of_v(orc):
+    q = np.zeros((3, 16), dtype=np.uint16)
+    k, v = rand_bf((37, 16), 4), rand_bf((37, 16), 5)
+    o = orc.attn_ref_fp64(q, k, v, range(3), 0.25)
+    want = np.array([math.fsum(f32(v)[:, c].astype(np.float64)) / 37 for c in range(16)])
+    assert np.allclose(o, want[None, :], rtol=1e-13, atol=1e-15)
+
+
+def test_ref_two_keys_logistic(orc):
+    q, k, v = rand_bf((4, 8), 6), rand_bf((2, 8), 7), rand_bf((2, 8), 8)
+    c = 0.3
+    o = orc.attn_ref_fp64(q, k, v, range(4), c)
+    qf, kf, vf = (f32(t).astype(np.float64) for t in (q, k, v))
+    for r in range(4):
+        z = c * (qf[r] @ kf[0] - qf[r] @ kf[1])
+        w0 = 1.0 / (1.0 + math.exp(-z))
+        assert np.allclose(o[r], w0 * vf[0] + (1 - w0) * vf[1], rtol=1e-12, atol=1e-14)
+
+
+def test_ref_rows_sum_to_one_and_shift_invariance(orc):
+    rng = np.random.default_rng(9)
+    q = exact_bf(rng.integers(-3, 4, size=(6, 16)))
+    k = exact_bf(rng.integers(-3, 4, size=(90, 16)))
+    ones = exact_bf(np.ones((90, 16)))
+    o = orc.attn_ref_fp64(q, k, ones, range(6), 0.37)
+    assert np.max(np.abs(o - 1.0)) <= 1e-12
+    # subtracting a per-channel vector from K shifts every score of a row by the same amount
+    mu = rng.integers(-5, 6, size=(1, 16))
+    ks = exact_bf(f32(k) - mu)
+    v = rand_bf((90, 16), 10)
+    a = orc.attn_ref_fp64(q, k, v, range(6), 0.37)
+    b = orc.attn_ref_fp64(q, ks, v, range(6), 0.37)
+    assert np.max(np.abs(a - b)) <= 1e-12 * np.max(np.abs(a))
+
+
+# -------------------------------------------------------------------------------------------- E exact case
+def _exact_case(seed, nkv=150, d=16, rows=(0, 3, 17, 63), tile=64):
+    """Scores are integers in [-7, 7] and scales are one, so every p = 2^(S - m) is exact in fp32, bf16
+    and (times 448) in E4M3; the result is a rational number known exactly."""
+    rng = np.random.default_rng(seed)
+    nq = 64
+    qc = np.zeros((nq, d), dtype=np.int8)
+    for r in range(nq):
+        idx = rng.choice(d, size=7, replace=False)
+        qc[r, idx] = rng.choice([-1, 1], size=7)
+    kc = rng.integers(-1, 2, size=(nkv, d)).astype(np.int8)
+    # the row maximum sits in the ragged last tile for row 3, in the first tile for row 17
+    kc[nkv - 1] = qc[3]
+    kc[1] = qc[17]
+    S = qc.astype(np.int64) @ kc.astype(np.int64).T
+    assert np.max(np.abs(S)) <= 7
+    return qc, kc, S, list(rows)
+
+
+def _expected(S_row, vhat):
+    """Exact softmax-in-base-2 weighted mean: sum_j 2^S_j v_j / sum_j 2^S_j, as fp64 of the exact rational."""
+    w = [Fraction(2) ** int(s) for s in S_row]
+    den = sum(w)
+    out = []
+    for c in range(vhat.shape[1]):
+        num = sum(wj * Fraction(float(vhat[j, c])) for j, wj in enumerate(w))
+        out.append(float(num / den))
+    return np.array(out)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("tile", [64, 32, 7])
+def test_emulate_exact_multi_tile(orc, mode, tile):
+    qc, kc, S, rows = _exact_case(11 + mode)
+    nkv, d = kc.shape
+    sm = unit_scale_sm()
+    rng = np.random.default_rng(5)
+    if mode == 2:
+        vcodes = rng.integers(0, 0x7E, size=(nkv, d)).astype(np.uint8) | (rng.integers(0, 2, size=(nkv, d)) << 7).astype(np.uint8)
+        vhat = orc.e4m3_decode(vcodes).astype(np.float64)
+        quant = dict(q_codes=qc, q_scales=np.ones(1, np.float32), k_codes=np.concatenate([kc, np.zeros((192 - nkv, d), np.int8)]),
+                     k_scales=np.ones(3, np.float32), v_codes=vcodes, v_scales=np.ones(d, np.float32))
+        got = orc.attn_emulate(2, rows, tile=tile, sm_scale=sm, blk_q=64, blk_k=64, nkv=nkv, quant=quant)
+    else:
+        vb = exact_bf(rng.integers(-16, 17, size=(nkv, d)) / 8.0)
+        vhat = f32(vb).astype(np.float64)
+        if mode == 1:
+            quant = dict(q_codes=qc, q_scales=np.ones(1, np.float32), k_codes=np.concatenate([kc, np.zeros((192 - nkv, d), np.int8)]),
+                         k_scales=np.ones(3, np.float32))
+            got = orc.attn_emulate(1, rows, tile=tile, sm_scale=sm, blk_q=64, blk_k=64, nkv=nkv, quant=quant, v_bf16=vb)
+        else:
+            got = orc.attn_emulate(0, rows, tile=tile, sm_scale=sm, blk_q=64, blk_k=64, nkv=nkv,
+                                   q_bf16=exact_bf(qc), k_bf16=exact_bf(kc), v_bf16=vb)
+    want = np.stack([bf_round(_expected(S[r], vhat)) for r in rows])
+    assert np.array_equal(got, want)
+
+
+# -------------------------------------------------------------------------------------------- E vs R
+def _ref_and_emulate(orc, mode, q, k, v, tile, sm, blk_q=64, blk_k=64, rows=None):
+    n = q.shape[0]
+    rows = list(range(n)) if rows is None else rows
+    R = orc.attn_ref_fp64(q, k, v, rows, sm)
+    if mode == 0:
+        E = orc.attn_emulate(0, rows, tile=tile, sm_scale=sm, blk_q=blk_q, blk_k=blk_k, nkv=k.shape[0],
+                             q_bf16=q, k_bf16=k, v_bf16=v)
+    else:
+        quant = orc.quantize_head(q, k, v, blk_q, blk_k, mode)
+        E = orc.attn_emulate(mode, rows, tile=tile, sm_scale=sm, blk_q=blk_q, blk_k=blk_k, nkv=k.shape[0],
+                             quant=quant, v_bf16=v)
+    return R, f32(E).astype(np.float64)
+
+
+def test_emulate_bf16_mode_within_rounding_of_ref(orc):
+    q, k, v = rand_bf((200, 64), 21), rand_bf((301, 64), 22, 2.0), rand_bf((301, 64), 23)
+    R, E = _ref_and_emulate(orc, 0, q, k, v, 64, 0.125)
+    # P rounded to bf16 moves each weight by <= 2^-9 relative; the output rounding adds <= 2^-9 |O|
+    vmax = np.max(np.abs(f32(v)))
+    bound = 2.0 ** -9 * vmax + 2.0 ** -8 * np.abs(R) + 1e-6
+    assert np.all(np.abs(E - R) <= bound)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_emulate_tile_width_only_moves_rounding(orc, mode):
+    q, k, v = rand_bf((64, 64), 31), rand_bf((150, 64), 32), rand_bf((150, 64), 33)
+    outs = [_ref_and_emulate(orc, mode, q, k, v, t, 0.125)[1] for t in (1, 7, 64, 150)]
+    vmax = np.max(np.abs(f32(v)))
+    step = 2.0 ** -4 if mode == 2 else 2.0 ** -8  # P rounding granularity relative to the running max
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) <= step * vmax
+
+
+@pytest.mark.parametrize("mode,rel", [(1, 0.04), (2, 0.07)])
+def test_emulate_quantized_modes_near_ref(orc, mode, rel):
+    q, k, v = rand_bf((128, 128), 41), rand_bf((500, 128), 42), rand_bf((500, 128), 43)
+    R, E = _ref_and_emulate(orc, mode, q, k, v, 64, 1 / math.sqrt(128), blk_q=128, blk_k=64)
+    err = np.linalg.norm(E - R) / np.linalg.norm(R)
+    cos = np.sum(E * R) / (np.linalg.norm(E) * np.linalg.norm(R))
+    assert err < rel and cos > 0.995, (err, cos)
+
+
+# -------------------------------------------------------------------------------------------- guard cases
+@pytest.mark.parametrize("mode", [1, 2])
+def test_constant_k_gives_uniform_attention(orc, mode):
+    # K constant per channel -> K' = 0 -> every K block guarded (scale 0) -> all scores 0 -> O = mean of V^
+    rng = np.random.default_rng(50)
+    k = exact_bf(np.repeat(rng.integers(-9, 10, size=(1, 32)), 96, axis=0))
+    q, v = rand_bf((64, 32), 51), rand_bf((96, 32), 52)
+    v = v.copy()
+    v[:, 5] = 0  # an all-zero V channel
+    quant = orc.quantize_head(q, k, v, 64, 64, mode)
+    assert np.all(quant["k_scales"] == 0)
+    E = orc.attn_emulate(mode, range(64), tile=64, sm_scale=0.2, blk_q=64, blk_k=64, nkv=96, quant=quant, v_bf16=v)
+    if mode == 1:
+        vhat = f32(v).astype(np.float64)
+        want = vhat.mean(axis=0)
+    else:
+        assert quant["v_scales"][5] == 0
+        vhat = orc.e4m3_decode(quant["v_codes"]).astype(np.float64)
+        want = vhat.mean(axis=0) * quant["v_scales"].astype(np.float64)
+    assert np.all(np.isfinite(f32(E)))
+    assert np.array_equal(E, np.repeat(bf_round(want)[None, :], 64, axis=0))
+    assert np.all(f32(E)[:, 5] == 0)
+
+
+def test_zero_query_block_gives_uniform_attention(orc):
+    q = rand_bf((128, 32), 60).copy()
+    q[64:] = 0
+    k, v = rand_bf((80, 32), 61), rand_bf((80, 32), 62)
+    quant = orc.quantize_head(q, k, v, 64, 64, 1)
+    assert quant["q_scales"][1] == 0
+    E = orc.attn_emulate(1, range(64, 128), tile=64, sm_scale=0.2, blk_q=64, blk_k=64, nkv=80, quant=quant, v_bf16=v)
+    want = bf_round(f32(v).astype(np.float64).mean(axis=0))
+    assert np.array_equal(E, np.repeat(want[None, :], 64, axis=0))
+
+
+def test_tiny_workload_zero_channel_is_finite_and_close(orc):
+    w = wl.WORKLOADS["tiny"]
+    for h in range(w.H):
+        q, k, v = (wl.bits(t) for t in wl.head_inputs(w, 0, h))
+        assert np.all(k[:, 0] == 0)
+        R, E = _ref_and_emulate(orc, 1, q, k, v, 64, w.sm_scale, w.blk_q, w.blk_k)
+        assert np.all(np.isfinite(E))
+        cos = np.sum(E * R) / (np.linalg.norm(E) * np.linalg.norm(R))
+        assert cos > 0.999
+
+
+def test_smoothing_keeps_quantized_output(orc):
+    # integer K with integer per-channel offsets: the mean absorbs the offset exactly, codes are equal,
+    # so the quantized output is bit-identical (the purpose of smoothing K)
+    rng = np.random.default_rng(70)
+    k = rng.integers(-6, 7, size=(130, 32)).astype(np.float32)
+    off = rng.integers(-40, 41, size=(1, 32)).astype(np.float32)
+    q, v = rand_bf((64, 32), 71), rand_bf((130, 32), 72)
+    outs = []
+    for kk in (k, k + off):
+        kb = exact_bf(kk)
+        quant = orc.quantize_head(q, kb, v, 64, 64, 2)
+        outs.append(orc.attn_emulate(2, range(64), tile=64, sm_scale=0.2, blk_q=64, blk_k=64, nkv=130, quant=quant))
+    assert np.array_equal(outs[0], outs[1])
