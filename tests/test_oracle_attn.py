@@ -256,3 +256,31 @@ def test_smoothing_keeps_quantized_output(orc):
         quant = orc.quantize_head(q, kb, v, 64, 64, 2)
         outs.append(orc.attn_emulate(2, range(64), tile=64, sm_scale=0.2, blk_q=64, blk_k=64, nkv=130, quant=quant))
     assert np.array_equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_emulate_p_rounding_closed_form(orc, mode):
+    # two keys with base-2 logits 0 and -1/2: p = (1, 2^-1/2).  P is rounded before P*V (bf16 in mode 1,
+    # E4M3 of 448*p in mode 2: 448 * 0.70710677 = 316.78 -> 320) while the denominator keeps the
+    # unrounded p, so O = (w0*v0 + w1*v1) / (1 + 2^-1/2) with (w0, w1) = (1, 0.70703125) or (448, 320)/448.
+    sm = unit_scale_sm()
+    d = 4
+    qc = np.zeros((64, d), np.int8)
+    qc[:, 0] = 1
+    kc = np.zeros((64, d), np.int8)
+    kc[1, 0] = -1
+    quant = dict(q_codes=qc, q_scales=np.ones(1, np.float32), k_codes=kc, k_scales=np.array([0.5], np.float32))
+    p1 = float(np.float32(2.0 ** -0.5))
+    if mode == 1:
+        vb = exact_bf([[1.0, 2.0, -3.0, 0.5], [4.0, -1.0, 0.25, 8.0]])
+        vhat = f32(vb).astype(np.float64)
+        w = (1.0, 0.70703125)
+        got = orc.attn_emulate(1, [0, 9], tile=64, sm_scale=sm, blk_q=64, blk_k=64, nkv=2, quant=quant, v_bf16=vb)
+    else:
+        vcodes = orc.e4m3_encode(np.array([[1.0, 2.0, -3.0, 0.5], [4.0, -1.0, 0.25, 8.0]], np.float32))
+        vhat = orc.e4m3_decode(vcodes).astype(np.float64)
+        quant.update(v_codes=vcodes, v_scales=np.ones(d, np.float32))
+        w = (1.0, 320.0 / 448.0)
+        got = orc.attn_emulate(2, [0, 9], tile=64, sm_scale=sm, blk_q=64, blk_k=64, nkv=2, quant=quant)
+    want = (w[0] * vhat[0] + w[1] * vhat[1]) / (1.0 + p1)
+    assert np.array_equal(got, np.repeat(bf_round(want)[None, :], 2, axis=0))
