@@ -1,0 +1,163 @@
+/*
+ * sattn.h -- C ABI of libsattn: SageAttention-style quantized attention for video diffusion
+ * transformers, hand-written HIP for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes, and where the pages describe it:
+ *   - Attention O = softmax(c * Q K^T) V per (batch, head) with no mask: the scaled-dot-product flash
+ *     attention operator that dominates the FLOP profile of a Wan-class image-to-video DiT (TMAP I2V
+ *     acceleration write-up, ai.aiking123.com/155823, section "Attention 性能优化 / 背景", FLOP table).
+ *   - It is replaced by an 8-bit quantized operator (same page, section "attention量化": SageAttention),
+ *     with the whole self-attention computation in 8 bits on Wan (section "显存优化 / 量化").
+ *   - Precision is chosen per attention layer (section "保持视频质量": layer-selective quantization),
+ *     which here is the per-call `mode` argument.
+ *   - Scales computed from an all-zero channel must not divide by zero (section "优化算子细节"): every
+ *     scale is guarded (amax < 2^-100 -> scale 0, codes 0).
+ *   - The score matrix is never materialised (tutorial "视频生成推理加速实战:从基线到27倍", step 3,
+ *     item "算子融合与高效注意力"): the softmax runs online over 64-key tiles.
+ *
+ * Quantization (modes 1 and 2), all in IEEE fp32 with round-to-nearest-even:
+ *   mean[c]   = per-channel mean of K over the Nkv tokens.  Summation order is fixed: 64-token runs summed
+ *               one value after another, then the run sums one after another, then one division by Nkv.
+ *   K'        = float(K) - mean  (not re-rounded)
+ *   Q, K'     : blocks of blk_q (Q) / blk_k (K') consecutive tokens of one (batch, head), all d channels;
+ *               a = max|x| over the block's valid tokens; a < 2^-100 -> scale 0 and codes 0; otherwise
+ *               scale = a/127, code = clamp(rint(x * (127/a)), -127, 127).
+ *   V (mode 2): per channel a_c = max over tokens |V[:,c]|; guard as above; scale = a_c/448,
+ *               code = E4M3FN(v * (448/a_c)) rounded to nearest even, saturating at 448.
+ * Attention (per 64-key tile, ascending): x = S_int * (s_q*s_k*c*log2 e) (mode 0: x = (q.k)*c*log2 e);
+ *   m' = max(m, max x); alpha = 2^(m-m'); p = 2^(x-m'); l = alpha*l + sum p;
+ *   acc = alpha*acc + P^ V^ with P^ = bf16(p) (modes 0/1) or E4M3(448 p) (mode 2) and V^ = V (bf16) or
+ *   the V codes (mode 2); O = acc / l (mode 2: acc * scale_v[c] / (448 l)), rounded to bf16.
+ *
+ * Conventions for every entry point:
+ *   - Pointers inside the structs are DEVICE pointers; the structs themselves and every other pointer
+ *     argument are HOST memory, read only during the call.
+ *   - Nothing is allocated and nothing is synchronised.  All work is enqueued on `stream` (0 = the null
+ *     stream) and the call returns.  Faults inside kernels surface at the caller's next synchronisation.
+ *   - The caller owns every buffer.  The library keeps no state between calls, so it is re-entrant;
+ *     concurrent calls need distinct workspaces and outputs.  Outputs must not alias inputs.
+ *   - Errors: arguments are checked on the host before any launch.  A bad argument returns
+ *     SATTN_ERR_INVALID_ARG, a valid but unsupported shape SATTN_ERR_UNSUPPORTED, a too small
+ *     workspace SATTN_ERR_WORKSPACE, a failed launch SATTN_ERR_HIP; in every error case nothing has
+ *     been enqueued.  No C++ exception crosses this interface.
+ *   - NaN or Inf inputs are outside the contract.  Zero blocks and zero channels are inside it and give
+ *     finite outputs.
+ */
+#ifndef SATTN_H
+#define SATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* sattn_stream_t; /* a hipStream_t */
+
+typedef enum {
+  SATTN_OK = 0,
+  SATTN_ERR_INVALID_ARG = 1,
+  SATTN_ERR_UNSUPPORTED = 2,
+  SATTN_ERR_WORKSPACE = 3,
+  SATTN_ERR_HIP = 4
+} sattn_status;
+
+typedef enum {
+  SATTN_MODE_BF16 = 0,    /* exact bf16 attention (bf16 QK^T and P*V, fp32 accumulation)        */
+  SATTN_MODE_I8_BF16 = 1, /* INT8 QK^T with int32 accumulation, bf16 P*V                         */
+  SATTN_MODE_I8_FP8 = 2   /* INT8 QK^T with int32 accumulation, FP8-E4M3 P*V                     */
+} sattn_mode;
+
+/* A bf16 activation tensor [B, H, N, d] addressed as ptr + b*stride_b + h*stride_h + n*stride_n + c
+ * (strides in elements; the channel stride is 1).  Both [B,H,N,d] and [B,N,H,d] storage fit.
+ * Requirements: ptr 16-byte aligned; stride_b, stride_h, stride_n multiples of 8; d in {64, 128}. */
+typedef struct {
+  void* ptr;
+  int B, H, N, d;
+  int64_t stride_b, stride_h, stride_n;
+} sattn_tensor;
+
+/* Quantized operands of one attention call.  nqb = ceil(Nq/blk_q), nkb = ceil(Nkv/64) (blk_k is 64),
+ * nq_pad = nqb*blk_q, nk_pad = nkb*64.  All arrays dense, device memory, owned by the caller.
+ *   q_codes  int8  [B, H, nq_pad, d]    row-major per token; pad tokens hold 0
+ *   q_scales fp32  [B, H, nqb]
+ *   k_codes  int8  [B, H, nk_pad, d]    codes of K' = K - mean; pad tokens hold 0
+ *   k_scales fp32  [B, H, nkb]
+ *   k_mean   fp32  [B, H, d]
+ *   v_codes  uint8 [B, H, nkb, d, 64]   mode 2: E4M3 codes of V, transposed per 64-key tile (element
+ *                                       (tile t, channel c, j) is key 64t+j); pad keys hold 0.  NULL otherwise.
+ *   v_scales fp32  [B, H, d]            mode 2 only (NULL otherwise)
+ *   v_t      bf16  [B, H, nkb, d, 64]   modes 0/1: V transposed per 64-key tile, same order as v_codes;
+ *                                       pad keys hold 0.  NULL in mode 2.
+ * sattn_quant_layout() fills every pointer from one base address. */
+typedef struct {
+  int B, H, Nq, Nkv, d, blk_q, blk_k, mode;
+  int8_t* q_codes;
+  float* q_scales;
+  int8_t* k_codes;
+  float* k_scales;
+  float* k_mean;
+  uint8_t* v_codes;
+  float* v_scales;
+  uint16_t* v_t;
+} sattn_quant;
+
+/* Status text for `st` (host pointer to static storage; never NULL). */
+const char* sattn_status_string(int st);
+
+/* Width of the key tiles over which the online softmax rescales (64 for every mode and d). */
+int sattn_kv_tile(int d, int mode);
+
+/* Bytes needed for the quantized operands of one call (the arrays of sattn_quant, each 256-byte
+ * aligned), or 0 if the shape is invalid. */
+size_t sattn_quant_bytes(int B, int H, int Nq, int Nkv, int d, int blk_q, int blk_k, int mode);
+
+/* Lays out the arrays of a sattn_quant inside `base` (device memory of at least sattn_quant_bytes).
+ * Pure host arithmetic, no device access.  Returns SATTN_ERR_INVALID_ARG for an invalid shape. */
+sattn_status sattn_quant_layout(int B, int H, int Nq, int Nkv, int d, int blk_q, int blk_k, int mode, void* base,
+                                sattn_quant* out);
+
+/* Workspace bytes for sattn_fwd / sattn_cross_fwd (the quantized operands plus the per-64-token
+ * partial sums of the K-mean and V-amax passes), or 0 if the shape is invalid. */
+size_t sattn_workspace_bytes(int B, int H, int Nq, int Nkv, int d, int blk_q, int blk_k, int mode);
+
+/* Scratch bytes needed by sattn_quantize (per-64-token K partial sums and V partial maxima). */
+size_t sattn_quantize_scratch_bytes(int B, int H, int Nkv, int d, int mode);
+
+/* Quantization of one attention call (modes 1 and 2), or the V transpose alone (mode 0).
+ * q: [B,H,Nq,d] bf16, k and v: [B,H,Nkv,d] bf16 (q may be NULL in mode 0).  `out` must describe
+ * buffers for the same shape and mode (e.g. from sattn_quant_layout).  `scratch` holds
+ * sattn_quantize_scratch_bytes bytes of device memory.  blk_q in {64, 128}; blk_k must be 64. */
+sattn_status sattn_quantize(const sattn_tensor* q, const sattn_tensor* k, const sattn_tensor* v, int mode,
+                            const sattn_quant* out, void* scratch, size_t scratch_bytes, sattn_stream_t stream);
+
+/* Attention on prepared operands: modes 1/2 read the codes in `qk` (q and k may be NULL); mode 0 reads
+ * q and k (bf16) and qk->v_t.  o: [B,H,Nq,d] bf16 output.  sm_scale <= 0 selects 1/sqrt(d). */
+sattn_status sattn_fwd_quantized(const sattn_tensor* q, const sattn_tensor* k, const sattn_quant* qk,
+                                 const sattn_tensor* o, float sm_scale, int mode, sattn_stream_t stream);
+
+/* Drop-in self-attention: quantize (or transpose V for mode 0) into `ws`, then attend.
+ * q, o: [B,H,Nq,d]; k, v: [B,H,Nkv,d]; ws: sattn_workspace_bytes(...) bytes of device memory. */
+sattn_status sattn_fwd(const sattn_tensor* q, const sattn_tensor* k, const sattn_tensor* v, const sattn_tensor* o,
+                       float sm_scale, int mode, int blk_q, int blk_k, void* ws, size_t ws_bytes,
+                       sattn_stream_t stream);
+
+/* Cross-attention of the video tokens (Nq long) over a short key sequence (Nkv small: e.g. 512 text +
+ * 257 image tokens of a Wan I2V block, one softmax over their concatenation).  Same arithmetic and
+ * workspace as sattn_fwd with blk_q = 128 and blk_k = 64. */
+sattn_status sattn_cross_fwd(const sattn_tensor* q, const sattn_tensor* k, const sattn_tensor* v,
+                             const sattn_tensor* o, float sm_scale, int mode, void* ws, size_t ws_bytes,
+                             sattn_stream_t stream);
+
+/* Test hook: the int32 scores S = q_codes . k_codes^T of one (b, h) for query rows [q0, q0+nq) and keys
+ * [k0, k0+nk), computed with the same INT8 matrix-core path as the attention kernel.
+ * out: device int32 [nq, nk] row-major.  Rows/keys must lie inside the padded code arrays. */
+sattn_status sattn_debug_qk_int32(const sattn_quant* qk, int b, int h, int q0, int nq, int k0, int nk,
+                                  int32_t* out, sattn_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SATTN_H */

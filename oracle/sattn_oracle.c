@@ -224,14 +224,26 @@ void orc_attn_emulate(int mode, int nkv, int d, int blk_q, int blk_k, int tile, 
                       const uint16_t* v_bf16, const uint8_t* v_codes, const float* v_scales,
                       const int* rows, int nrows, uint16_t* out, float* out_f32) {
   const float clog2e = sm_scale * 1.4426950408889634f; /* c * log2(e) in fp32 */
+  /* V^ as numbers: the bf16 values (modes 0/1) or the decoded E4M3 codes (mode 2) */
+  float* vhat = (float*)malloc(sizeof(float) * (size_t)nkv * d);
+  for (long long i = 0; i < (long long)nkv * d; ++i)
+    vhat[i] = (mode == 2) ? orc_e4m3_decode(v_codes[i]) : orc_bf16_to_f32(v_bf16[i]);
+  /* mode 0 reads the keys as numbers */
+  float* kf = NULL;
+  if (mode == 0) {
+    kf = (float*)malloc(sizeof(float) * (size_t)nkv * d);
+    for (long long i = 0; i < (long long)nkv * d; ++i) kf[i] = orc_bf16_to_f32(k_bf16[i]);
+  }
 #pragma omp parallel
   {
     float* x = (float*)malloc(sizeof(float) * (size_t)tile);
     double* acc = (double*)malloc(sizeof(double) * (size_t)d);
-    float* vrow = (float*)malloc(sizeof(float) * (size_t)d);
+    float* qrow = (float*)malloc(sizeof(float) * (size_t)d);
 #pragma omp for schedule(dynamic, 1)
     for (int ri = 0; ri < nrows; ++ri) {
       const int r = rows[ri];
+      if (mode == 0)
+        for (int c = 0; c < d; ++c) qrow[c] = orc_bf16_to_f32(q_bf16[(long long)r * d + c]);
       float m = -INFINITY;
       double l = 0.0;
       for (int c = 0; c < d; ++c) acc[c] = 0.0;
@@ -243,8 +255,7 @@ void orc_attn_emulate(int mode, int nkv, int d, int blk_q, int blk_k, int tile, 
           float xv;
           if (mode == 0) {
             double s = 0.0;
-            for (int c = 0; c < d; ++c)
-              s += (double)orc_bf16_to_f32(q_bf16[(long long)r * d + c]) * (double)orc_bf16_to_f32(k_bf16[(long long)j * d + c]);
+            for (int c = 0; c < d; ++c) s += (double)qrow[c] * (double)kf[(long long)j * d + c];
             xv = (float)s * clog2e;
           } else {
             int64_t s = 0;
@@ -263,15 +274,10 @@ void orc_attn_emulate(int mode, int nkv, int d, int blk_q, int blk_k, int tile, 
         for (int j = j0; j < j1; ++j) {
           const float p = (float)exp2((double)x[j - j0] - (double)mnew);
           psum += (double)p;
-          double ph;
-          if (mode == 2) {
-            ph = (double)orc_e4m3_decode(orc_e4m3_encode(p * 448.0f));
-            for (int c = 0; c < d; ++c) vrow[c] = orc_e4m3_decode(v_codes[(long long)j * d + c]);
-          } else {
-            ph = (double)orc_bf16_to_f32(orc_bf16_from_f32(p));
-            for (int c = 0; c < d; ++c) vrow[c] = orc_bf16_to_f32(v_bf16[(long long)j * d + c]);
-          }
-          for (int c = 0; c < d; ++c) acc[c] += ph * (double)vrow[c];
+          const double ph = (mode == 2) ? (double)orc_e4m3_decode(orc_e4m3_encode(p * 448.0f))
+                                        : (double)orc_bf16_to_f32(orc_bf16_from_f32(p));
+          const float* vj = vhat + (long long)j * d;
+          for (int c = 0; c < d; ++c) acc[c] += ph * (double)vj[c];
         }
         l = alpha * l + psum;
         m = mnew;
@@ -286,8 +292,10 @@ void orc_attn_emulate(int mode, int nkv, int d, int blk_q, int blk_k, int tile, 
     }
     free(x);
     free(acc);
-    free(vrow);
+    free(qrow);
   }
+  free(vhat);
+  free(kf);
 }
 
 /* ------------------------------------------------------------------------------------------------ */
@@ -296,33 +304,43 @@ void orc_attn_emulate(int mode, int nkv, int d, int blk_q, int blk_k, int tile, 
 /* ------------------------------------------------------------------------------------------------ */
 void orc_attn_ref_fp64(int nkv, int d, double sm_scale, const uint16_t* q_bf16, const uint16_t* k_bf16,
                        const uint16_t* v_bf16, const int* rows, int nrows, double* out) {
+  double* kd = (double*)malloc(sizeof(double) * (size_t)nkv * d);
+  double* vd = (double*)malloc(sizeof(double) * (size_t)nkv * d);
+  for (long long i = 0; i < (long long)nkv * d; ++i) {
+    kd[i] = orc_bf16_to_f32(k_bf16[i]);
+    vd[i] = orc_bf16_to_f32(v_bf16[i]);
+  }
 #pragma omp parallel
   {
     double* s = (double*)malloc(sizeof(double) * (size_t)nkv);
+    double* qd = (double*)malloc(sizeof(double) * (size_t)d);
+    double* num = (double*)malloc(sizeof(double) * (size_t)d);
 #pragma omp for schedule(dynamic, 1)
     for (int ri = 0; ri < nrows; ++ri) {
       const int r = rows[ri];
+      for (int c = 0; c < d; ++c) qd[c] = orc_bf16_to_f32(q_bf16[(long long)r * d + c]);
       double mx = -INFINITY;
       for (int j = 0; j < nkv; ++j) {
         double dot = 0.0;
-        for (int c = 0; c < d; ++c)
-          dot += (double)orc_bf16_to_f32(q_bf16[(long long)r * d + c]) * (double)orc_bf16_to_f32(k_bf16[(long long)j * d + c]);
+        for (int c = 0; c < d; ++c) dot += qd[c] * kd[(long long)j * d + c];
         s[j] = sm_scale * dot;
         if (s[j] > mx) mx = s[j];
       }
       double den = 0.0;
+      for (int c = 0; c < d; ++c) num[c] = 0.0;
       for (int j = 0; j < nkv; ++j) {
-        s[j] = exp(s[j] - mx);
-        den += s[j];
+        const double w = exp(s[j] - mx);
+        den += w;
+        for (int c = 0; c < d; ++c) num[c] += w * vd[(long long)j * d + c];
       }
-      for (int c = 0; c < d; ++c) {
-        double num = 0.0;
-        for (int j = 0; j < nkv; ++j) num += s[j] * (double)orc_bf16_to_f32(v_bf16[(long long)j * d + c]);
-        out[(long long)ri * d + c] = num / den;
-      }
+      for (int c = 0; c < d; ++c) out[(long long)ri * d + c] = num[c] / den;
     }
     free(s);
+    free(qd);
+    free(num);
   }
+  free(kd);
+  free(vd);
 }
 
 int orc_max_threads(void) {

@@ -1,0 +1,252 @@
+"""ctypes binding of libsattn (include/sattn.h) with the same entry-point names, plus torch marshalling.
+
+Every step of the computation runs in the HIP kernels of libsattn.so; this module only turns torch tensors
+into pointers, sizes and the current HIP stream, and raises ``SattnError`` for a non-OK status.  There is
+no CPU fallback: if the library is missing, importing the entry points fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsattn.so")
+
+SATTN_OK = 0
+SATTN_ERR_INVALID_ARG = 1
+SATTN_ERR_UNSUPPORTED = 2
+SATTN_ERR_WORKSPACE = 3
+SATTN_ERR_HIP = 4
+
+SATTN_MODE_BF16 = 0
+SATTN_MODE_I8_BF16 = 1
+SATTN_MODE_I8_FP8 = 2
+
+
+class SattnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {sattn_status_string(status)} (status {status})")
+
+
+class sattn_tensor(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("B", ctypes.c_int), ("H", ctypes.c_int), ("N", ctypes.c_int),
+                ("d", ctypes.c_int), ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64),
+                ("stride_n", ctypes.c_int64)]
+
+
+class sattn_quant(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("Nq", ctypes.c_int), ("Nkv", ctypes.c_int),
+                ("d", ctypes.c_int), ("blk_q", ctypes.c_int), ("blk_k", ctypes.c_int), ("mode", ctypes.c_int),
+                ("q_codes", ctypes.c_void_p), ("q_scales", ctypes.c_void_p), ("k_codes", ctypes.c_void_p),
+                ("k_scales", ctypes.c_void_p), ("k_mean", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+                ("v_scales", ctypes.c_void_p), ("v_t", ctypes.c_void_p)]
+
+
+_lib = None
+
+# (name, restype, argtypes) for every symbol declared in include/sattn.h
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+_TP = ctypes.POINTER(sattn_tensor)
+_QP = ctypes.POINTER(sattn_quant)
+SYMBOLS = [
+    ("sattn_status_string", ctypes.c_char_p, [_I]),
+    ("sattn_kv_tile", _I, [_I, _I]),
+    ("sattn_quant_bytes", _SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
+    ("sattn_quant_layout", _I, [_I, _I, _I, _I, _I, _I, _I, _I, _P, _QP]),
+    ("sattn_workspace_bytes", _SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
+    ("sattn_quantize_scratch_bytes", _SZ, [_I, _I, _I, _I, _I]),
+    ("sattn_quantize", _I, [_TP, _TP, _TP, _I, _QP, _P, _SZ, _P]),
+    ("sattn_fwd_quantized", _I, [_TP, _TP, _QP, _TP, ctypes.c_float, _I, _P]),
+    ("sattn_fwd", _I, [_TP, _TP, _TP, _TP, ctypes.c_float, _I, _I, _I, _P, _SZ, _P]),
+    ("sattn_cross_fwd", _I, [_TP, _TP, _TP, _TP, ctypes.c_float, _I, _P, _SZ, _P]),
+    ("sattn_debug_qk_int32", _I, [_QP, _I, _I, _I, _I, _I, _I, _P, _P]),
+]
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m quantized_attention_05_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, res, args in SYMBOLS:
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+# ------------------------------------------------------------------------------------- raw entry points
+def sattn_status_string(st: int) -> str:
+    return lib().sattn_status_string(int(st)).decode()
+
+
+def sattn_kv_tile(d: int, mode: int) -> int:
+    return int(lib().sattn_kv_tile(d, mode))
+
+
+def sattn_quant_bytes(B, H, Nq, Nkv, d, blk_q, blk_k, mode) -> int:
+    return int(lib().sattn_quant_bytes(B, H, Nq, Nkv, d, blk_q, blk_k, mode))
+
+
+def sattn_workspace_bytes(B, H, Nq, Nkv, d, blk_q, blk_k, mode) -> int:
+    return int(lib().sattn_workspace_bytes(B, H, Nq, Nkv, d, blk_q, blk_k, mode))
+
+
+def sattn_quantize_scratch_bytes(B, H, Nkv, d, mode) -> int:
+    return int(lib().sattn_quantize_scratch_bytes(B, H, Nkv, d, mode))
+
+
+def _check(st: int, where: str):
+    if st != SATTN_OK:
+        raise SattnError(st, where)
+
+
+def sattn_quant_layout(B, H, Nq, Nkv, d, blk_q, blk_k, mode, base: int) -> sattn_quant:
+    out = sattn_quant()
+    _check(lib().sattn_quant_layout(B, H, Nq, Nkv, d, blk_q, blk_k, mode, ctypes.c_void_p(base), ctypes.byref(out)),
+           "sattn_quant_layout")
+    return out
+
+
+def sattn_quantize(q, k, v, mode, out: sattn_quant, scratch: int, scratch_bytes: int, stream: int):
+    _check(lib().sattn_quantize(_ref(q), _ref(k), _ref(v), mode, ctypes.byref(out), ctypes.c_void_p(scratch),
+                                scratch_bytes, ctypes.c_void_p(stream)), "sattn_quantize")
+
+
+def sattn_fwd_quantized(q, k, qk: sattn_quant, o, sm_scale, mode, stream: int):
+    _check(lib().sattn_fwd_quantized(_ref(q), _ref(k), ctypes.byref(qk), _ref(o), float(sm_scale), mode,
+                                     ctypes.c_void_p(stream)), "sattn_fwd_quantized")
+
+
+def sattn_fwd(q, k, v, o, sm_scale, mode, blk_q, blk_k, ws: int, ws_bytes: int, stream: int):
+    _check(lib().sattn_fwd(_ref(q), _ref(k), _ref(v), _ref(o), float(sm_scale), mode, blk_q, blk_k,
+                           ctypes.c_void_p(ws), ws_bytes, ctypes.c_void_p(stream)), "sattn_fwd")
+
+
+def sattn_cross_fwd(q, k, v, o, sm_scale, mode, ws: int, ws_bytes: int, stream: int):
+    _check(lib().sattn_cross_fwd(_ref(q), _ref(k), _ref(v), _ref(o), float(sm_scale), mode, ctypes.c_void_p(ws),
+                                 ws_bytes, ctypes.c_void_p(stream)), "sattn_cross_fwd")
+
+
+def sattn_debug_qk_int32(qk: sattn_quant, b, h, q0, nq, k0, nk, out: int, stream: int):
+    _check(lib().sattn_debug_qk_int32(ctypes.byref(qk), b, h, q0, nq, k0, nk, ctypes.c_void_p(out),
+                                      ctypes.c_void_p(stream)), "sattn_debug_qk_int32")
+
+
+def _ref(t):
+    return None if t is None else ctypes.byref(t)
+
+
+# ------------------------------------------------------------------------------------- torch marshalling
+def tensor_desc(t: torch.Tensor | None) -> sattn_tensor | None:
+    """sattn_tensor for a 4-D bf16 device tensor indexed [B, H, N, d] (any strides with d contiguous)."""
+    if t is None:
+        return None
+    if t.dtype != torch.bfloat16 or t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("expected a 4-D bf16 tensor [B, H, N, d] with contiguous channels")
+    B, H, N, d = t.shape
+    return sattn_tensor(t.data_ptr(), B, H, N, d, t.stride(0), t.stride(1), t.stride(2))
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _resolve(sm_scale, d):
+    return 0.0 if sm_scale is None else float(sm_scale)
+
+
+def fwd(q, k, v, mode=SATTN_MODE_I8_FP8, sm_scale=None, blk_q=128, blk_k=64, out=None, workspace=None):
+    """Self-attention through sattn_fwd.  q, k, v: [B, H, N, d] bf16 on the GPU.  Returns O like q."""
+    B, H, Nq, d = q.shape
+    Nkv = k.shape[2]
+    o = torch.empty_like(q) if out is None else out
+    need = sattn_workspace_bytes(B, H, Nq, Nkv, d, blk_q, blk_k, mode)
+    if need == 0:
+        raise SattnError(SATTN_ERR_UNSUPPORTED, "sattn_workspace_bytes")
+    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=q.device)
+    sattn_fwd(tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(o), _resolve(sm_scale, d), mode, blk_q, blk_k,
+              ws.data_ptr(), ws.numel(), _stream())
+    return o
+
+
+def cross_fwd(q, k, v, mode=SATTN_MODE_BF16, sm_scale=None, out=None, workspace=None):
+    """Cross-attention through sattn_cross_fwd (short key sequence).  Returns O like q."""
+    B, H, Nq, d = q.shape
+    Nkv = k.shape[2]
+    o = torch.empty_like(q) if out is None else out
+    need = sattn_workspace_bytes(B, H, Nq, Nkv, d, 128, 64, mode)
+    if need == 0:
+        raise SattnError(SATTN_ERR_UNSUPPORTED, "sattn_workspace_bytes")
+    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=q.device)
+    sattn_cross_fwd(tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(o), _resolve(sm_scale, d), mode,
+                    ws.data_ptr(), ws.numel(), _stream())
+    return o
+
+
+class Quantized:
+    """Quantized operands in one device buffer, with torch views of each array (see sattn_quant)."""
+
+    def __init__(self, B, H, Nq, Nkv, d, blk_q, mode, device, blk_k=64):
+        self.shape = (B, H, Nq, Nkv, d, blk_q, blk_k, mode)
+        nbytes = sattn_quant_bytes(B, H, Nq, Nkv, d, blk_q, blk_k, mode)
+        if nbytes == 0:
+            raise SattnError(SATTN_ERR_UNSUPPORTED, "sattn_quant_bytes")
+        self.buf = torch.zeros(nbytes + 256, dtype=torch.uint8, device=device)
+        base = (self.buf.data_ptr() + 255) // 256 * 256
+        self.desc = sattn_quant_layout(B, H, Nq, Nkv, d, blk_q, blk_k, mode, base)
+        self._base = base
+        nqb, nkb = -(-Nq // blk_q), -(-Nkv // 64)
+        self.nqb, self.nkb = nqb, nkb
+        self.mode = mode
+
+        def view(ptr, numel, dtype, shape):
+            if not ptr:
+                return None
+            off = ptr - self.buf.data_ptr()
+            nb = numel * torch.tensor([], dtype=dtype).element_size()
+            return self.buf[off:off + nb].view(dtype).view(shape)
+
+        D = self.desc
+        self.q_codes = view(D.q_codes, B * H * nqb * blk_q * d, torch.int8, (B, H, nqb * blk_q, d))
+        self.q_scales = view(D.q_scales, B * H * nqb, torch.float32, (B, H, nqb))
+        self.k_codes = view(D.k_codes, B * H * nkb * 64 * d, torch.int8, (B, H, nkb * 64, d))
+        self.k_scales = view(D.k_scales, B * H * nkb, torch.float32, (B, H, nkb))
+        self.k_mean = view(D.k_mean, B * H * d, torch.float32, (B, H, d))
+        self.v_codes = view(D.v_codes, B * H * nkb * d * 64, torch.uint8, (B, H, nkb, d, 64))
+        self.v_scales = view(D.v_scales, B * H * d, torch.float32, (B, H, d))
+        self.v_t = view(D.v_t, B * H * nkb * d * 64, torch.int16, (B, H, nkb, d, 64))
+
+
+def quantize(q, k, v, mode=SATTN_MODE_I8_FP8, blk_q=128, quant: Quantized | None = None):
+    """Run sattn_quantize; returns a ``Quantized`` holding the codes/scales (device tensors)."""
+    B, H, Nq, d = q.shape
+    Nkv = k.shape[2]
+    qz = quant if quant is not None else Quantized(B, H, Nq, Nkv, d, blk_q, mode, q.device)
+    sb = sattn_quantize_scratch_bytes(B, H, Nkv, d, mode)
+    scratch = torch.empty(max(sb, 1), dtype=torch.uint8, device=q.device)
+    sattn_quantize(tensor_desc(q), tensor_desc(k), tensor_desc(v), mode, qz.desc, scratch.data_ptr(), sb, _stream())
+    qz._scratch = scratch  # keep alive until the stream has used it
+    return qz
+
+
+def fwd_quantized(qz: Quantized, q=None, k=None, sm_scale=None, out=None, Nq_like=None):
+    """Attention on prepared operands through sattn_fwd_quantized."""
+    B, H, Nq, Nkv, d, blk_q, blk_k, mode = qz.shape
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device=qz.buf.device)
+    sattn_fwd_quantized(tensor_desc(q), tensor_desc(k), qz.desc, tensor_desc(out), _resolve(sm_scale, d), mode,
+                        _stream())
+    return out
+
+
+def debug_qk_int32(qz: Quantized, b, h, q0, nq, k0, nk):
+    out = torch.empty((nq, nk), dtype=torch.int32, device=qz.buf.device)
+    sattn_debug_qk_int32(qz.desc, b, h, q0, nq, k0, nk, out.data_ptr(), _stream())
+    return out

@@ -1,0 +1,107 @@
+"""Shared helpers of the GPU parity tests: seeded inputs, runs through the C ABI, oracle references and the
+comparison metrics.  The GPU side only ever receives the generated bf16 tensors; every expected value
+comes from ``oracle``."""
+from __future__ import annotations
+
+import functools
+import math
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from quantized_attention_05_amd import sattn
+from quantized_attention_05_amd import workloads as wl
+
+REL_L2_GATE = 2e-3   # GPU output vs the oracle's step-by-step emulation
+COS_GATE = 0.999     # GPU output vs fp64 exact attention, where the emulation itself reaches it
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@functools.lru_cache(maxsize=2)
+def host_inputs(w: wl.Workload, seed: int | None = None):
+    return wl.full_inputs(w, seed)
+
+
+def device_inputs(w: wl.Workload, seed: int | None = None, layout: str = "bhnd"):
+    q, k, v = host_inputs(w, seed)
+    if layout == "bhnd":
+        return tuple(t.cuda() for t in (q, k, v))
+    # [B, N, H, d] storage, viewed as [B, H, N, d]
+    return tuple(t.transpose(1, 2).contiguous().cuda().transpose(1, 2) for t in (q, k, v))
+
+
+def head_bits(w: wl.Workload, b: int, h: int, seed: int | None = None):
+    q, k, v = host_inputs(w, seed)
+    return wl.bits(q[b, h]), wl.bits(k[b, h]), wl.bits(v[b, h])
+
+
+def u16(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def f32(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits).astype(np.uint32) << 16).view(np.float32)
+
+
+def untile_v(tiled: np.ndarray) -> np.ndarray:
+    """[nkb, d, 64] per-tile transposed layout -> [nkb*64, d] natural layout."""
+    nkb, d, t = tiled.shape
+    return tiled.transpose(0, 2, 1).reshape(nkb * t, d)
+
+
+def sample_rows(nq: int, blk: int = 128) -> np.ndarray:
+    """First, middle and last (ragged) query blocks."""
+    nqb = -(-nq // blk)
+    blocks = sorted({0, nqb // 2, nqb - 1})
+    rows = np.concatenate([np.arange(b * blk, min((b + 1) * blk, nq)) for b in blocks])
+    return rows.astype(np.int32)
+
+
+def sample_heads(H: int):
+    return sorted({0, H // 2, H - 1})
+
+
+def oracle_quant(w: wl.Workload, b: int, h: int, mode: int, blk_q: int, seed=None):
+    q, k, v = head_bits(w, b, h, seed)
+    return oracle.quantize_head(q, k, v, blk_q, 64, mode)
+
+
+def oracle_outputs(w: wl.Workload, b: int, h: int, mode: int, rows, blk_q: int, sm_scale: float, seed=None):
+    """(E as fp32 values of its bf16 output, R in fp64) for the given rows of one head."""
+    q, k, v = head_bits(w, b, h, seed)
+    if mode == 0:
+        E = oracle.attn_emulate(0, rows, tile=64, sm_scale=sm_scale, blk_q=blk_q, blk_k=64, nkv=w.Nkv,
+                                q_bf16=q, k_bf16=k, v_bf16=v)
+    else:
+        qz = oracle.quantize_head(q, k, v, blk_q, 64, mode)
+        E = oracle.attn_emulate(mode, rows, tile=64, sm_scale=sm_scale, blk_q=blk_q, blk_k=64, nkv=w.Nkv,
+                                quant=qz, v_bf16=v)
+    R = oracle.attn_ref_fp64(q, k, v, rows, sm_scale)
+    return f32(E).astype(np.float64), R
+
+
+def metrics(gpu: np.ndarray, E: np.ndarray, R: np.ndarray):
+    gpu = gpu.astype(np.float64)
+    rel = float(np.linalg.norm(gpu - E) / max(np.linalg.norm(E), 1e-300))
+    cos = float(np.sum(gpu * R) / max(np.linalg.norm(gpu) * np.linalg.norm(R), 1e-300))
+    cos_e = float(np.sum(E * R) / max(np.linalg.norm(E) * np.linalg.norm(R), 1e-300))
+    return rel, cos, cos_e
+
+
+def check_output(gpu_rows: np.ndarray, E: np.ndarray, R: np.ndarray, label: str):
+    assert np.all(np.isfinite(gpu_rows)), f"{label}: non-finite output"
+    rel, cos, cos_e = metrics(gpu_rows, E, R)
+    say(f"  {label}: rel-L2 vs emulation {rel:.3e}, cos vs fp64 {cos:.6f} (emulation {cos_e:.6f})")
+    assert rel <= REL_L2_GATE, f"{label}: rel-L2 {rel:.3e} > {REL_L2_GATE}"
+    # the cosine gate applies where the method itself (the emulation) reaches it
+    if cos_e >= COS_GATE:
+        assert cos >= COS_GATE - 1e-4, f"{label}: cosine {cos:.6f}"
+    else:
+        assert cos >= cos_e - 1e-4, f"{label}: cosine {cos:.6f} below the emulation's {cos_e:.6f}"
+    return rel, cos
