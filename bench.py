@@ -1,0 +1,220 @@
+"""Benchmark of the quantized self-attention hot path on one MI355X.
+
+One step = one ``sattn_fwd`` call (quantization of Q/K/V followed by the fused attention kernel) on the
+Wan-14B 720p self-attention shape (B=1, H=40, N=75600 latent tokens, d=128), INT8 Q*K^T + FP8-E4M3 P*V,
+inputs resident in HBM.  Prints one JSON line with the effective attention throughput
+(4*Nq*Nkv*d*H ops per call), the roofline position of the attention kernel (timed alone with HIP events on
+the stream it runs on) and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective attention TOPS + % INT8 MFMA peak, Wan-14B 720p self-attn"
+PEAK_TOPS = {0: 2500.0, 1: 5000.0, 2: 5000.0}  # dense MFMA peak of the kernel's dominant op (bf16 / int8+fp8)
+INT8_PEAK_TOPS = 5000.0
+HBM_PEAK_GBPS = 8000.0
+MODE_DTYPE = {0: "bf16", 1: "int8+bf16", 2: "int8+fp8e4m3"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "quantized_attention_05_amd", "csrc", f) for f in ("attn.hip", "sattn_internal.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, mode: int, launches_ops: float):
+    """HBM bytes per launch of the attention kernel from committed rocprofv3 counter runs, or None when the
+    counters were taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = table.get(f"{workload}/mode{mode}")
+    if not rec or rec.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return {"fetch_bytes": rec["fetch_bytes"], "write_bytes": rec["write_bytes"],
+            "total_bytes": rec["fetch_bytes"] + rec["write_bytes"], "source": rec.get("source", TRAFFIC_FILE)}
+
+
+def cpu_baseline(w, mode: int, budget_s: float):
+    """The oracle, as it stands, on a bounded sample: quantize one head in full, then emulate query blocks of
+    that head until about `budget_s` seconds of CPU time are spent.  Extrapolated linearly to the whole call
+    (H heads x all query rows) and reported as effective TOPS."""
+    import numpy as np
+
+    import oracle
+    from quantized_attention_05_amd import workloads as wl
+
+    q, k, v = (wl.bits(t) for t in wl.head_inputs(w, 0, 0))
+    t0 = time.perf_counter()
+    quant = oracle.quantize_head(q, k, v, w.blk_q, w.blk_k, mode) if mode != 0 else None
+    t_quant = time.perf_counter() - t0
+    nqb = -(-w.Nq // w.blk_q)
+    order = [0, nqb - 1] + [int(i) for i in np.linspace(1, nqb - 2, 64).astype(int)]
+    rows_done, t_attn, blocks = 0, 0.0, []
+    for blk in order:
+        rows = np.arange(blk * w.blk_q, min((blk + 1) * w.blk_q, w.Nq), dtype=np.int32)
+        t0 = time.perf_counter()
+        if mode == 0:
+            oracle.attn_emulate(0, rows, tile=64, sm_scale=w.sm_scale, blk_q=w.blk_q, blk_k=w.blk_k, nkv=w.Nkv,
+                                q_bf16=q, k_bf16=k, v_bf16=v)
+        else:
+            oracle.attn_emulate(mode, rows, tile=64, sm_scale=w.sm_scale, blk_q=w.blk_q, blk_k=w.blk_k, nkv=w.Nkv,
+                                quant=quant, v_bf16=v)
+        t_attn += time.perf_counter() - t0
+        rows_done += rows.size
+        blocks.append(blk)
+        if t_quant + t_attn >= budget_s:
+            break
+    t_call = w.H * w.B * (t_quant + t_attn * (w.Nq / rows_done))
+    return {
+        "value": w.ops / t_call / 1e12,
+        "unit": "TOPS",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": (f"head 0 of {w.name}: full quantization ({t_quant:.2f} s) + step-by-step emulation of "
+                   f"{rows_done} query rows in {len(blocks)} blocks against all {w.Nkv} keys ({t_attn:.2f} s); "
+                   f"extrapolated to {w.B * w.H} heads x {w.Nq} rows = {t_call:.1f} s per call"),
+        "seconds_measured": round(t_quant + t_attn, 2),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan14b-720p")
+    ap.add_argument("--mode", type=int, default=2, choices=[0, 1, 2])
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=None, help="attention-kernel-only timing reps")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the attention of one (batch, head) never "
+                                   "leaves its GPU, and no multi-GPU path is built; run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+
+    from quantized_attention_05_amd import sattn
+    from quantized_attention_05_amd import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    mode = args.mode
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.perf_counter()
+    q, k, v = wl.full_inputs(w)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    gen_s = time.perf_counter() - t0
+    o = torch.empty_like(q)
+    ws_bytes = sattn.sattn_workspace_bytes(w.B, w.H, w.Nq, w.Nkv, w.d, w.blk_q, w.blk_k, mode)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        sattn.fwd(q, k, v, mode=mode, sm_scale=w.sm_scale, blk_q=w.blk_q, blk_k=w.blk_k, out=o, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    value = w.ops / (ms_per_step * 1e-3) / 1e12
+
+    # the dominant kernel alone: attention on prepared operands, HIP events on the same stream
+    qz = sattn.Quantized(w.B, w.H, w.Nq, w.Nkv, w.d, w.blk_q, mode, dev)
+    sattn.quantize(q, k, v, mode=mode, blk_q=w.blk_q, quant=qz)
+    qarg = q if mode == 0 else None
+    karg = k if mode == 0 else None
+    reps = args.kernel_reps or max(5, args.steps)
+    for _ in range(2):
+        sattn.fwd_quantized(qz, qarg, karg, sm_scale=w.sm_scale, out=o)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        sattn.fwd_quantized(qz, qarg, karg, sm_scale=w.sm_scale, out=o)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    attn_ms = e0.elapsed_time(e1) / reps
+    # quantization alone (HBM-bound): algorithmic bytes = read Q, K, V (bf16) + write codes
+    e0.record(stream)
+    for _ in range(reps):
+        sattn.quantize(q, k, v, mode=mode, blk_q=w.blk_q, quant=qz)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    quant_ms = e0.elapsed_time(e1) / reps
+    elems_q, elems_kv = w.B * w.H * w.Nq * w.d, w.B * w.H * w.Nkv * w.d
+    if mode == 0:
+        quant_bytes = elems_kv * 2 * 2                       # V read + transposed V written
+    elif mode == 1:
+        quant_bytes = (elems_q + 2 * elems_kv) * 2 + elems_q + elems_kv + elems_kv * 2
+    else:
+        quant_bytes = (elems_q + 2 * elems_kv) * 2 + elems_q + 2 * elems_kv
+
+    achieved = w.ops / (attn_ms * 1e-3) / 1e12
+    traffic = measured_traffic(w.name, mode, w.ops)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": MODE_DTYPE[mode],
+        "data": "synthetic: seeded Wan-shaped N(0,1) Q/K/V, K per-channel offsets, zeroed K blocks (recipe in DESIGN.md)",
+        "config": {"workload": f"{w.name} self-attention" if "cross" not in w.name else f"{w.name} attention",
+                   "B": w.B, "H": w.H, "Nq": w.Nq, "Nkv": w.Nkv, "d": w.d, "mode": wl.MODE_NAMES[mode],
+                   "blk_q": w.blk_q, "blk_k": w.blk_k, "parallelism": "single GPU"},
+        "pct_int8_mfma_peak": round(100.0 * value / INT8_PEAK_TOPS, 2),
+        "attn_kernel_ms": round(attn_ms, 4),
+        "quantize_ms": round(quant_ms, 4),
+        "quantize_gbps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_TOPS[mode],
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_TOPS[mode], 4),
+            "traffic": traffic,
+            "kernel": f"attn_kernel<mode {mode}, d {w.d}>",
+            "ops_per_launch": w.ops,
+        },
+        "wall_s_timed_region": round(wall, 3),
+        "input_generation_s": round(gen_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, mode, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
