@@ -1,7 +1,7 @@
 // Fused attention kernels of libsattn for CDNA4 (gfx950).
 //
 // One workgroup = 4 waves = 128 query rows of one (batch, head); each wave owns 32 rows.  The workgroup
-// streams 64-key tiles of K and V through LDS (double-buffered) and every wave, per tile:
+// streams 64-key tiles of K and V through LDS and every wave, per tile:
 //   1. S^T = K Q^T on the matrix cores: INT8 v_mfma_i32_32x32x32_i8 with int32 accumulation (modes 1, 2),
 //      or bf16 v_mfma_f32_32x32x16_bf16 (mode 0).  Computing the transpose puts one query per lane
 //      (lanes n and n+32 share query n), so the softmax row statistics are lane-local plus one swap.
@@ -11,9 +11,14 @@
 //      per-tile scale s_q*s_k*c*log2 e), skipping the O rescale when no running max moved.
 //   3. Round P (bf16, or E4M3 of 448*p) straight into the B operand of the P*V matrix-core op
 //      (v_mfma_f32_32x32x16_bf16 or v_mfma_f32_32x32x64_f8f6f4 reading E4M3), accumulating O^T in fp32.
-// The score matrix never leaves registers (tutorial "视频生成推理加速实战:从基线到27倍", step 3, item
-// "算子融合与高效注意力"); 8-bit Q*K^T and P*V follow the TMAP I2V write-up (sections "attention量化",
-// "显存优化 / 量化"); the per-call mode is its layer-selective precision (section "保持视频质量").
+// K/V tiles move HBM -> LDS with global_load_lds_dwordx4 (no register staging), two stages, one barrier
+// per tile; the LDS rows are XOR-swizzled in 16-byte granules so that every matrix-operand read is free of
+// bank conflicts.  The score matrix never leaves registers (tutorial "视频生成推理加速实战:从基线到27倍",
+// step 3, item "算子融合与高效注意力"); 8-bit Q*K^T and P*V follow the TMAP I2V write-up (sections
+// "attention量化", "显存优化 / 量化"); the per-call mode is its layer-selective precision (section
+// "保持视频质量").
+#include <type_traits>
+
 #include "sattn_internal.h"
 
 namespace sattn {
@@ -24,6 +29,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;
@@ -38,84 +44,52 @@ struct AttnArg {
   int nqt;             // query tiles of 128 rows per (b, h)
 };
 
-// Row slot i (0..31) of a 32-row operand block maps to the element whose output lands in register
-// order for lane half g: slot i = 8a + 4g + t  ->  element 32g*(half size) + 4a + t (see callers).
-__device__ __forceinline__ int slot_key(int i, int bm) {  // key inside a 64-key tile, M-block bm (0, 1)
+// Operand row slot i (0..31) of a 32-row block, i = 8a + 4g + t, is fed the element that lands in
+// register 4a + t of lane half g of the 32x32 output, so lane (n, g) holds elements 32g.. (keys) or
+// (D/2)g.. (channels) in register order.
+__device__ __forceinline__ int slot_key(int i, int bm) {  // key inside a 64-key tile, 32-key block bm
   return 32 * ((i >> 2) & 1) + 16 * bm + 4 * (i >> 3) + (i & 3);
 }
 template <int D>
-__device__ __forceinline__ int slot_channel(int i, int cb) {  // channel, output block cb (0 .. D/32-1)
+__device__ __forceinline__ int slot_channel(int i, int cb) {  // channel, 32-channel output block cb
   return (D / 2) * ((i >> 2) & 1) + 16 * cb + 4 * (i >> 3) + (i & 3);
 }
 
-// LDS geometry (bytes); rows padded by 16 bytes against bank conflicts.
+// XOR swizzles of the 16-byte granules of an LDS row (G granules per row).  For the row sets that the 16
+// lanes of a quarter-wave (and the 8 lanes of an eighth) read together, they map equal logical granules
+// to distinct bank groups, for 32 and for 64 LDS banks.
+template <int G>
+__device__ __forceinline__ int kswz(int key) {
+  if (G == 4) return (((key >> 1) & 1) ^ ((key >> 2) & 1)) | (((key >> 5) & 1) << 1);
+  if (G == 8) return ((key & 1) ^ ((key >> 2) & 1)) | (((key >> 1) & 1) << 1) | (((key >> 5) & 1) << 2);
+  return (key & 3) | (((key >> 5) & 1) << 2) | (((key >> 2) & 1) << 3);
+}
+template <int G, int D>
+__device__ __forceinline__ int vswz(int ch) {
+  constexpr int gb = (D == 128) ? 6 : 5;  // channel bit that selects the lane half
+  if (G == 4) return (((ch >> 1) & 1) ^ ((ch >> 2) & 1)) | (((ch >> gb) & 1) << 1);
+  return ((ch & 1) ^ ((ch >> 2) & 1)) | (((ch >> 1) & 1) << 1) | (((ch >> gb) & 1) << 2);
+}
+
 template <int MODE, int D>
-struct Lds {
-  static constexpr int KB = (MODE == 0) ? 2 : 1;           // bytes per K element
-  static constexpr int VB = (MODE == 2) ? 1 : 2;           // bytes per V element
-  static constexpr int KROW = D * KB + 16;                 // one key
-  static constexpr int VROW = kTile * VB + 16;             // one channel (transposed V)
+struct Geo {
+  static constexpr int KB = (MODE == 0) ? 2 : 1;  // bytes per K element
+  static constexpr int VB = (MODE == 2) ? 1 : 2;  // bytes per V element
+  static constexpr int KROW = D * KB;             // bytes of one key row
+  static constexpr int VROW = kTile * VB;         // bytes of one (transposed) V channel row
+  static constexpr int KG = KROW / 16;            // granules per K row
+  static constexpr int VG = VROW / 16;            // granules per V row
   static constexpr int KBYTES = kTile * KROW;
   static constexpr int VBYTES = D * VROW;
   static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int KPIECES = kTile * D * KB / 16;      // 16-byte pieces per tile
-  static constexpr int VPIECES = D * kTile * VB / 16;
-  static constexpr int PIECES = KPIECES + VPIECES;
-  static constexpr int PPT = PIECES / 256;                 // pieces per thread
-  static_assert(PIECES % 256 == 0, "tile pieces must split evenly over 256 threads");
-};
-
-// Global -> registers for tile t (prefetch), then registers -> LDS.
-template <int MODE, int D>
-struct TileLoader {
-  using L = Lds<MODE, D>;
-  uint4 r[L::PPT];
-
-  __device__ __forceinline__ void load(const AttnArg& a, int64_t bh, int b, int h, int t) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < L::PPT; ++i) {
-      const int p = tid + 256 * i;
-      if (p < L::KPIECES) {
-        if (MODE == 0) {
-          constexpr int PPR = D * 2 / 16;                   // pieces per key row
-          const int key = p / PPR, col = (p % PPR) * 8;     // col in elements
-          const int j = t * kTile + key;
-          if (j < a.qa.Nkv) {
-            r[i] = *reinterpret_cast<const uint4*>(a.k.ptr + b * a.k.sb + h * a.k.sh + (int64_t)j * a.k.sn + col);
-          } else {
-            r[i] = make_uint4(0, 0, 0, 0);
-          }
-        } else {
-          const int8_t* src = a.qa.k_codes + (bh * a.qa.nkb + t) * (int64_t)(kTile * D);
-          r[i] = *reinterpret_cast<const uint4*>(src + (int64_t)p * 16);
-        }
-      } else {
-        const int pv = p - L::KPIECES;
-        const uint8_t* src = (MODE == 2) ? a.qa.v_codes : reinterpret_cast<const uint8_t*>(a.qa.v_t);
-        src += (bh * a.qa.nkb + t) * (int64_t)(D * kTile * L::VB);
-        r[i] = *reinterpret_cast<const uint4*>(src + (int64_t)pv * 16);
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(uint8_t* stage) const {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < L::PPT; ++i) {
-      const int p = tid + 256 * i;
-      if (p < L::KPIECES) {
-        constexpr int PPR = D * L::KB / 16;
-        const int key = p / PPR, col = (p % PPR) * 16;
-        *reinterpret_cast<uint4*>(stage + key * L::KROW + col) = r[i];
-      } else {
-        const int pv = p - L::KPIECES;
-        constexpr int PPR = kTile * L::VB / 16;
-        const int ch = pv / PPR, col = (pv % PPR) * 16;
-        *reinterpret_cast<uint4*>(stage + L::KBYTES + ch * L::VROW + col) = r[i];
-      }
-    }
-  }
+  static constexpr int KIPW = KBYTES / (16 * 256);  // load instructions per wave for K (4 waves x 64 lanes)
+  static constexpr int VIPW = VBYTES / (16 * 256);
+  static constexpr int IPW = KIPW + VIPW;
+  static constexpr int KSTEPS = (MODE == 0) ? D / 16 : D / 32;  // k-steps of the Q*K^T op
+  static constexpr int CB = D / 32;                              // 32-channel output blocks
+  static constexpr int VREADS = (MODE == 2) ? 2 : 4;             // 16-byte V reads per output block
+  static_assert(KBYTES % (16 * 256) == 0 && VBYTES % (16 * 256) == 0, "tiles split into whole instructions");
+  static_assert(2 * STAGE <= 65536, "LDS offsets must fit the 16-bit instruction offset");
 };
 
 // The workgroup -> (query tile, head, batch) map.  Workgroups are handed to the 8 XCDs round-robin; this
@@ -127,91 +101,10 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
   return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
 }
 
-// Online softmax of one 64-key tile for the wave's 32 queries, then P*V.  sf holds the raw scores
-// (S as float; lane (n, g) register r of block bm is key 32g + 16bm + r of the tile).  f = scale of the
-// tile (s_q*s_k*c*log2 e), so x = S*f.  TAIL: keys at or beyond `valid` are outside the sequence.
-template <int MODE, int D, bool TAIL>
-__device__ __forceinline__ void softmax_pv(v16f (&sf)[2], float f, int valid, int n, int g, const uint8_t* vl,
-                                           float& m, float& l, v16f (&oacc)[D / 32]) {
-  using L = Lds<MODE, D>;
-  constexpr int CB = D / 32;
-  auto in_seq = [&](int bm, int r) { return !TAIL || (32 * g + 16 * bm + r < valid); };
-  float smax = -3.0e38f;
-#pragma unroll
-  for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (in_seq(bm, r)) smax = fmaxf(smax, sf[bm][r]);
-  // f >= 0 and rounding is monotone, so the tile max of x is f times the max of S.  A lane half with no
-  // key inside the sequence contributes -3e38*f <= 0, which never exceeds the other half's value
-  // (for f = 0 every x is 0).
-  float xmax = smax * f;
-  xmax = fmaxf(xmax, __shfl_xor(xmax, 32, 64));
-  const float mnew = fmaxf(m, xmax);
-  if (__any(mnew != m)) {
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // 0 on the first tile (m = -inf)
-    l *= alpha;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
-  }
-  m = mnew;
-  // mode 2 stores 448 p (= 2^(x - m + log2 448)) so the E4M3 conversion needs no extra multiply
-  const float nb = ((MODE == 2) ? 8.807354922057604f : 0.0f) - mnew;
-
-  if (MODE == 2) {
-    v8i pf;  // E4M3 of 448 p for keys 32g .. 32g+31 (byte j <-> key 32g + j)
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const int bm = w >> 2, r0 = 4 * (w & 3);
-      float p[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sf[bm][r0 + e], f, nb));
-        if (!in_seq(bm, r0 + e)) p[e] = 0.0f;
-        l += p[e];
-      }
-      int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-      word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
-      pf[w] = word;
-    }
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const int ch = slot_channel<D>(n, cb);
-      const v8i vv = *reinterpret_cast<const v8i*>(vl + ch * L::VROW + 32 * g);
-      oacc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vv, pf, oacc[cb], 0, 0, 0, 0, 0, 0);
-    }
-  } else {
-    v8bf pb[4];  // bf16 p: operand j holds keys 32g + 8j .. 32g + 8j + 7
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int bm = j >> 1, r0 = 8 * (j & 1);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sf[bm][r0 + e], f, nb));
-        if (!in_seq(bm, r0 + e)) p = 0.0f;
-        l += p;
-        pb[j][e] = (__bf16)p;
-      }
-    }
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const int ch = slot_channel<D>(n, cb);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const v8bf vv = *reinterpret_cast<const v8bf*>(vl + ch * L::VROW + (32 * g + 8 * j) * 2);
-        oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[j], oacc[cb], 0, 0, 0);
-      }
-    }
-  }
-}
-
 template <int MODE, int D>
 __global__ void __launch_bounds__(256, 2) attn_kernel(AttnArg a) {
-  using L = Lds<MODE, D>;
-  constexpr int KSTEPS = (MODE == 0) ? D / 16 : D / 32;  // K-dim steps of the QK^T op
-  constexpr int CB = D / 32;                              // 32-channel output blocks
+  using G = Geo<MODE, D>;
+  constexpr int CB = G::CB;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -221,20 +114,83 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(AttnArg a) {
   const int64_t bh = (int64_t)b * a.qa.H + h;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int n = lane & 31;          // query of this lane inside the wave's 32 rows
-  const int g = lane >> 5;          // lane half
+  const int n = lane & 31;  // query of this lane inside the wave's 32 rows
+  const int g = lane >> 5;  // lane half
   const int q0 = qt * kRowsPerWG + wave * kRowsPerWave;
   const bool active = q0 < a.qa.Nq;
+  const int nkb = a.qa.nkb;
+  const int Nkv = a.qa.Nkv;
+
+  // ---- per-lane load plan: instruction j of this wave fills LDS granules [(4j + wave) * 64, +64)
+  int ld_off[G::IPW];  // byte offset inside the tile's source (K rows of mode 0: key and column instead)
+  int ld_key[G::KIPW];
+#pragma unroll
+  for (int j = 0; j < G::IPW; ++j) {
+    const int slot = (4 * j + wave) * 64 + lane;
+    if (j < G::KIPW) {
+      const int key = slot / G::KG, phys = slot % G::KG;
+      const int col = phys ^ kswz<G::KG>(key);
+      ld_key[j] = key;
+      ld_off[j] = (MODE == 0) ? col * 16 : key * G::KROW + col * 16;
+    } else {
+      const int s = slot - G::KBYTES / 16;
+      const int ch = s / G::VG, phys = s % G::VG;
+      const int col = phys ^ vswz<G::VG, D>(ch);
+      ld_off[j] = ch * G::VROW + col * 16;
+    }
+  }
+  const uint8_t* ksrc = (MODE == 0) ? reinterpret_cast<const uint8_t*>(a.k.ptr + b * a.k.sb + h * a.k.sh)
+                                    : reinterpret_cast<const uint8_t*>(a.qa.k_codes) + bh * nkb * (int64_t)G::KBYTES;
+  const uint8_t* vsrc = ((MODE == 2) ? a.qa.v_codes : reinterpret_cast<const uint8_t*>(a.qa.v_t)) +
+                        bh * nkb * (int64_t)G::VBYTES;
+
+  auto issue_tile = [&](int t, int stage) {
+    uint8_t* dst = smem + stage * G::STAGE;
+#pragma unroll
+    for (int j = 0; j < G::IPW; ++j) {
+      const uint8_t* src;
+      if (j < G::KIPW) {
+        if (MODE == 0) {
+          const int row = min(t * kTile + ld_key[j], Nkv - 1);  // rows past the sequence are masked later
+          src = ksrc + (int64_t)row * a.k.sn * 2 + ld_off[j];
+        } else {
+          src = ksrc + (int64_t)t * G::KBYTES + ld_off[j];
+        }
+      } else {
+        src = vsrc + (int64_t)t * G::VBYTES + ld_off[j];
+      }
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(dst + (4 * j + wave) * 64 * 16), 16, 0, 0);
+    }
+  };
+
+  // ---- per-lane LDS read offsets of the matrix operands (within a stage)
+  int k_rd[2][G::KSTEPS];
+#pragma unroll
+  for (int bm = 0; bm < 2; ++bm) {
+    const int key = slot_key(n, bm);
+#pragma unroll
+    for (int s = 0; s < G::KSTEPS; ++s) k_rd[bm][s] = key * G::KROW + (((2 * s + g) ^ kswz<G::KG>(key)) * 16);
+  }
+  int v_rd[CB][G::VREADS];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int ch = slot_channel<D>(n, cb);
+#pragma unroll
+    for (int e = 0; e < G::VREADS; ++e) {
+      const int c = (MODE == 2) ? 2 * g + e : 4 * g + e;
+      v_rd[cb][e] = G::KBYTES + ch * G::VROW + ((c ^ vswz<G::VG, D>(ch)) * 16);
+    }
+  }
 
   // ---- Q fragment (B operand of S^T = K Q^T), resident for the whole key loop
-  v4i qf8[MODE == 0 ? 1 : KSTEPS];
-  v8bf qfb[MODE == 0 ? KSTEPS : 1];
+  v4i qf8[MODE == 0 ? 1 : G::KSTEPS];
+  v8bf qfb[MODE == 0 ? G::KSTEPS : 1];
   float fq = 0.0f;  // s_q * c * log2(e)
   if (MODE == 0) {
     const int row = q0 + n;
     const uint16_t* src = a.q.ptr + b * a.q.sb + h * a.q.sh + (int64_t)row * a.q.sn;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
+    for (int s = 0; s < G::KSTEPS; ++s) {
       if (active && row < a.qa.Nq) qfb[s] = *reinterpret_cast<const v8bf*>(src + 16 * s + 8 * g);
       else qfb[s] = (v8bf){};
     }
@@ -243,66 +199,150 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(AttnArg a) {
     if (active) {
       const int8_t* src = a.qa.q_codes + (bh * a.qa.nqb * a.qa.blk_q + q0 + n) * D;
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) qf8[s] = *reinterpret_cast<const v4i*>(src + 32 * s + 16 * g);
+      for (int s = 0; s < G::KSTEPS; ++s) qf8[s] = *reinterpret_cast<const v4i*>(src + 32 * s + 16 * g);
       fq = a.qa.q_scales[bh * a.qa.nqb + q0 / a.qa.blk_q] * a.clog2e;
     } else {
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) qf8[s] = (v4i){};
+      for (int s = 0; s < G::KSTEPS; ++s) qf8[s] = (v4i){};
     }
   }
+  const float* kscale = a.qa.k_scales + bh * nkb;
 
   v16f oacc[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) oacc[cb] = (v16f){};
   float m = -INFINITY;  // running max of x for query n (identical in both lane halves)
-  float l = 0.0f;       // this lane's half of the running sum of p (or 448 p in mode 2)
+  float l = 0.0f;       // this lane's half of the running sum of p (mode 2: of 448 p)
 
-  const int nkb = a.qa.nkb;
-  TileLoader<MODE, D> ld;
-  ld.load(a, bh, b, h, 0);
-  ld.store(smem);
-  __syncthreads();
+  auto process = [&](const uint8_t* st, int t, auto tail_tag) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    const int valid = Nkv - t * kTile;  // keys of this tile inside the sequence (>= 64 unless TAIL)
+    auto in_seq = [&](int bm, int r) { return !TAIL || (32 * g + 16 * bm + r < valid); };
 
-  for (int t = 0; t < nkb; ++t) {
-    uint8_t* stage = smem + (t & 1) * L::STAGE;
-    if (t + 1 < nkb) ld.load(a, bh, b, h, t + 1);
-
-    // ---------------- 1. S^T tile: two 32-key blocks x 32 queries
-    v16f sf[2];
-    {
-      const uint8_t* kl = stage;
+    // ---------------- 1. scores of 64 keys x 32 queries: two independent accumulation chains
+    float sf[2][16];
+    float smax;
+    if (MODE == 0) {
+      v16f acc[2] = {(v16f){}, (v16f){}};
 #pragma unroll
-      for (int bm = 0; bm < 2; ++bm) {
-        const int key = slot_key(n, bm);  // this lane's operand row (row slot n, half g)
-        if (MODE == 0) {
-          v16f acc = {};
+      for (int s = 0; s < G::KSTEPS; ++s)
 #pragma unroll
-          for (int s = 0; s < KSTEPS; ++s) {
-            const v8bf kv = *reinterpret_cast<const v8bf*>(kl + key * L::KROW + (16 * s + 8 * g) * 2);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qfb[s], acc, 0, 0, 0);
-          }
-          sf[bm] = acc;
-        } else {
-          v16i acc = {};
-#pragma unroll
-          for (int s = 0; s < KSTEPS; ++s) {
-            const v4i kv = *reinterpret_cast<const v4i*>(kl + key * L::KROW + 32 * s + 16 * g);
-            acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kv, qf8[s], acc, 0, 0, 0);
-          }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sf[bm][r] = (float)acc[r];  // exact: |S| < 2^24
+        for (int bm = 0; bm < 2; ++bm) {
+          const v8bf kv = *reinterpret_cast<const v8bf*>(st + k_rd[bm][s]);
+          acc[bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qfb[s], acc[bm], 0, 0, 0);
         }
-      }
+      smax = -3.0e38f;
+#pragma unroll
+      for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sf[bm][r] = acc[bm][r];
+          if (in_seq(bm, r)) smax = fmaxf(smax, sf[bm][r]);
+        }
+    } else {
+      v16i acc[2] = {(v16i){}, (v16i){}};
+#pragma unroll
+      for (int s = 0; s < G::KSTEPS; ++s)
+#pragma unroll
+        for (int bm = 0; bm < 2; ++bm) {
+          const v4i kv = *reinterpret_cast<const v4i*>(st + k_rd[bm][s]);
+          acc[bm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kv, qf8[s], acc[bm], 0, 0, 0);
+        }
+      int imax = -0x7FFFFFFF;
+#pragma unroll
+      for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (in_seq(bm, r)) imax = max(imax, acc[bm][r]);
+#pragma unroll
+      for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sf[bm][r] = (float)acc[bm][r];  // exact: |S| < 2^24
+      smax = (float)imax;  // a half with no key in the sequence gives -2^31, scaled below like the rest
     }
 
-    // ---------------- 2./3. online softmax and P*V
-    const float f = (MODE == 0) ? fq : fq * a.qa.k_scales[bh * nkb + t];
-    const int valid = a.qa.Nkv - t * kTile;
-    if (valid < kTile) softmax_pv<MODE, D, true>(sf, f, valid, n, g, stage + L::KBYTES, m, l, oacc);
-    else softmax_pv<MODE, D, false>(sf, f, valid, n, g, stage + L::KBYTES, m, l, oacc);
+    // ---------------- 2. online softmax (base 2).  x = S*f with f >= 0; rounding is monotone, so the
+    // tile max of x is f times the max of S.  A lane half without keys contributes a value <= 0 that never
+    // exceeds the other half's (for f = 0 every x is 0).
+    const float f = (MODE == 0) ? fq : fq * kscale[t];
+    float xmax = smax * f;
+    xmax = fmaxf(xmax, __shfl_xor(xmax, 32, 64));
+    const float mnew = fmaxf(m, xmax);
+    if (__any(mnew != m)) {
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // 0 on the first tile (m = -inf)
+      l *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+    }
+    m = mnew;
+    // mode 2 keeps 448 p (= 2^(x - m + log2 448)) so that the E4M3 conversion needs no multiply
+    const float nb = ((MODE == 2) ? 8.807354922057604f : 0.0f) - mnew;
+    float lp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 
-    if (t + 1 < nkb) ld.store(smem + ((t + 1) & 1) * L::STAGE);
+    // ---------------- 3. P rounded into the P*V operand, then P*V
+    if (MODE == 2) {
+      v8i pf;  // E4M3 of 448 p for keys 32g .. 32g+31 (byte j <-> key 32g + j)
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const int bm = w >> 2, r0 = 4 * (w & 3);
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sf[bm][r0 + e], f, nb));
+          if (!in_seq(bm, r0 + e)) p[e] = 0.0f;
+          lp[e] += p[e];
+        }
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
+        pf[w] = word;
+      }
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const v4i lo = *reinterpret_cast<const v4i*>(st + v_rd[cb][0]);
+        const v4i hi = *reinterpret_cast<const v4i*>(st + v_rd[cb][1]);
+        const v8i vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        oacc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vv, pf, oacc[cb], 0, 0, 0, 0, 0, 0);
+      }
+    } else {
+      v8bf pb[4];  // bf16 p: operand j holds keys 32g + 8j .. 32g + 8j + 7
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int bm = j >> 1, r0 = 8 * (j & 1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sf[bm][r0 + e], f, nb));
+          if (!in_seq(bm, r0 + e)) p = 0.0f;
+          lp[e & 3] += p;
+          pb[j][e] = (__bf16)p;
+        }
+      }
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const v8bf vv = *reinterpret_cast<const v8bf*>(st + v_rd[cb][j]);
+          oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[j], oacc[cb], 0, 0, 0);
+        }
+    }
+    l += (lp[0] + lp[1]) + (lp[2] + lp[3]);
+  };
+
+  // ---- main loop over the tiles that lie wholly inside the sequence (one barrier per tile; the next
+  // tile's loads fly while this one is computed), then the ragged last tile, if any, on its own path
+  const int nfull = Nkv / kTile;
+  issue_tile(0, 0);
+  for (int t = 0; t < nfull; ++t) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // tile t visible to all waves; everyone is done with the other stage
+    if (t + 1 < nkb) issue_tile(t + 1, (t + 1) & 1);
+    process(smem + (t & 1) * G::STAGE, t, std::false_type{});
+  }
+  if (nfull < nkb) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    process(smem + (nfull & 1) * G::STAGE, nfull, std::true_type{});
   }
 
   // ---------------- epilogue: O = acc / l  (mode 2: acc * s_v[c] / (448 l)), bf16, lane writes D/2 channels
@@ -335,8 +375,8 @@ template <int D>
 __global__ void __launch_bounds__(64) debug_qk_kernel(QuantArg qa, int64_t bh, int q0, int nq, int k0, int nk,
                                                        int32_t* out) {
   constexpr int KSTEPS = D / 32;
-  __shared__ __attribute__((aligned(16))) uint8_t kl[kTile * (D + 16)];
   constexpr int KROW = D + 16;
+  __shared__ __attribute__((aligned(16))) uint8_t kl[kTile * KROW];
   const int lane = threadIdx.x, n = lane & 31, g = lane >> 5;
   const int rq = q0 + blockIdx.x * 32;  // first query row of this block
   const int rk = k0 + blockIdx.y * 64;  // first key of this block
@@ -374,8 +414,7 @@ __global__ void __launch_bounds__(64) debug_qk_kernel(QuantArg qa, int64_t bh, i
 
 template <int MODE, int D>
 hipError_t launch_attn_t(const AttnArg& a, int nwg, hipStream_t s) {
-  using L = Lds<MODE, D>;
-  constexpr int bytes = 2 * L::STAGE;
+  constexpr int bytes = 2 * Geo<MODE, D>::STAGE;
   static bool configured = false;
   if (!configured) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<MODE, D>),

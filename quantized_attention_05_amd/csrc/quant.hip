@@ -139,12 +139,28 @@ __global__ void __launch_bounds__(128) kv_finalize_kernel(QuantArg qa, bool with
   const int c = (int)(i % d);
   const float* ps = ksum + bh * qa.nkb * d + c;
   float total = 0.0f;
-  for (int r = 0; r < qa.nkb; ++r) total = total + ps[(int64_t)r * d];
+  int r = 0;
+  // the loads of 16 run sums are issued together; the additions stay one after another in run order
+  for (; r + 16 <= qa.nkb; r += 16) {
+    float x[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) x[u] = ps[(int64_t)(r + u) * d];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) total = total + x[u];
+  }
+  for (; r < qa.nkb; ++r) total = total + ps[(int64_t)r * d];
   qa.k_mean[i] = total / (float)qa.Nkv;
   if (with_v) {
     const float* pm = vmax + bh * qa.nkb * d + c;
     float a = 0.0f;
-    for (int r = 0; r < qa.nkb; ++r) a = fmaxf(a, pm[(int64_t)r * d]);
+    for (r = 0; r + 16 <= qa.nkb; r += 16) {
+      float x[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) x[u] = pm[(int64_t)(r + u) * d];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) a = fmaxf(a, x[u]);
+    }
+    for (; r < qa.nkb; ++r) a = fmaxf(a, pm[(int64_t)r * d]);
     const bool zero = !(a >= kGuard);
     qa.v_scales[i] = zero ? 0.0f : a / 448.0f;
     vinv[i] = zero ? 0.0f : 448.0f / a;
