@@ -50,6 +50,62 @@ def measured_traffic(workload: str, mode: int, launches_ops: float):
             "total_bytes": rec["fetch_bytes"] + rec["write_bytes"], "source": rec.get("source", TRAFFIC_FILE)}
 
 
+def layer_selective(args):
+    """The layer-selective pass: 40 self-attention calls on fresh tensors in a fixed seeded per-layer mode
+    pattern (8 layers bf16, 32 layers INT8+FP8), each followed by a cross-attention call over 769 keys.
+    Values do not change the timing, so the tensors are drawn on the GPU (torch generator seeded per layer)."""
+    import torch
+
+    from quantized_attention_05_amd import sattn
+    from quantized_attention_05_amd import workloads as wl
+
+    ws_ = wl.WORKLOADS["layersel-720p-self"]
+    wc_ = wl.WORKLOADS["layersel-720p-cross"]
+    modes = wl.layer_modes()
+    dev = torch.device("cuda:0")
+    shape_q = (ws_.B, ws_.H, ws_.Nq, ws_.d)
+    shape_c = (wc_.B, wc_.H, wc_.Nkv, wc_.d)
+    layers = []
+    for i in range(wl.LAYERSEL_LAYERS):
+        gen = torch.Generator(device=dev).manual_seed(ws_.seed + i)
+        q, k, v = (torch.randn(shape_q, generator=gen, device=dev).to(torch.bfloat16) for _ in range(3))
+        genc = torch.Generator(device=dev).manual_seed(wc_.seed + i)
+        kc, vc = (torch.randn(shape_c, generator=genc, device=dev).to(torch.bfloat16) for _ in range(2))
+        layers.append((q, k, v, kc, vc))
+    o = torch.empty(shape_q, dtype=torch.bfloat16, device=dev)
+    ws_bytes = max(sattn.sattn_workspace_bytes(ws_.B, ws_.H, ws_.Nq, ws_.Nkv, ws_.d, 128, 64, m) for m in range(3))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    def one_pass():
+        for (q, k, v, kc, vc), m in zip(layers, modes):
+            sattn.fwd(q, k, v, mode=m, sm_scale=ws_.sm_scale, out=o, workspace=ws)
+            sattn.cross_fwd(q, kc, vc, mode=0, sm_scale=wc_.sm_scale, out=o, workspace=ws)
+
+    for _ in range(args.warmup):
+        one_pass()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        one_pass()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    ops = wl.LAYERSEL_LAYERS * (ws_.ops + wc_.ops)
+    print(json.dumps({
+        "metric": "effective attention TOPS, layer-selective Wan-14B 720p pass (40 self + 40 cross calls)",
+        "value": round(ops / (ms * 1e-3) / 1e12, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8+fp8e4m3 / bf16 per layer",
+        "data": "synthetic: N(0,1) drawn on the GPU, torch generator seeded per layer",
+        "config": {"workload": "layer-selective pass", "layers": wl.LAYERSEL_LAYERS,
+                   "modes": "".join(str(m) for m in modes), "self": [ws_.H, ws_.Nq, ws_.d],
+                   "cross_nkv": wc_.Nkv, "cross_mode": "bf16"},
+        "pct_int8_mfma_peak": round(100.0 * ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2),
+    }), flush=True)
+
+
 def cpu_baseline(w, mode: int, budget_s: float):
     """The oracle, as it stands, on a bounded sample: quantize one head in full, then emulate query blocks of
     that head until about `budget_s` seconds of CPU time are spent.  Extrapolated linearly to the whole call
@@ -98,17 +154,34 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="wan14b-720p")
+    ap.add_argument("--workload", default="wan14b-720p",
+                    help="a name from quantized_attention_05_amd.workloads.WORKLOADS, or 'layersel'")
     ap.add_argument("--mode", type=int, default=2, choices=[0, 1, 2])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=None, help="attention-kernel-only timing reps")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run one plain 256 MiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
+
+    if args.calibrate_copy:
+        import torch
+
+        x = torch.full((1 << 28,), 1, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": x.numel()}))
+        return
 
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the attention of one (batch, head) never "
                                    "leaves its GPU, and no multi-GPU path is built; run with --gpus 1"}))
         sys.exit(2)
+    if args.workload == "layersel":
+        layer_selective(args)
+        return
 
     import torch
 
@@ -177,7 +250,7 @@ def main():
         quant_bytes = (elems_q + 2 * elems_kv) * 2 + elems_q + 2 * elems_kv
 
     achieved = w.ops / (attn_ms * 1e-3) / 1e12
-    traffic = measured_traffic(w.name, mode, w.ops)
+    traffic_detail = measured_traffic(w.name, mode, w.ops)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -204,7 +277,8 @@ def main():
             "peak": PEAK_TOPS[mode],
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_TOPS[mode], 4),
-            "traffic": traffic,
+            "traffic": traffic_detail["total_bytes"] if traffic_detail else None,
+            "traffic_detail": traffic_detail,
             "kernel": f"attn_kernel<mode {mode}, d {w.d}>",
             "ops_per_launch": w.ops,
         },
