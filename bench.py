@@ -279,7 +279,7 @@ def main():
             "frac": round(achieved / PEAK_TOPS[mode], 4),
             "traffic": traffic_detail["total_bytes"] if traffic_detail else None,
             "traffic_detail": traffic_detail,
-            "kernel": f"attn_kernel<mode {mode}, d {w.d}>",
+            "kernel": (f"attn_kernel<0, {w.d}>" if mode == 0 else f"attn_pipe_kernel<{mode}, {w.d}, 4>"),
             "ops_per_launch": w.ops,
         },
         "wall_s_timed_region": round(wall, 3),

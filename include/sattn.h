@@ -71,7 +71,9 @@ typedef enum {
 
 /* A bf16 activation tensor [B, H, N, d] addressed as ptr + b*stride_b + h*stride_h + n*stride_n + c
  * (strides in elements; the channel stride is 1).  Both [B,H,N,d] and [B,N,H,d] storage fit.
- * Requirements: ptr 16-byte aligned; stride_b, stride_h, stride_n multiples of 8; d in {64, 128}. */
+ * Requirements: ptr 16-byte aligned; stride_b, stride_h, stride_n multiples of 8; d in {64, 128}.
+ * In mode 0 (bf16 scores) the attention kernel addresses the K rows of a 64-key tile with 32-bit offsets, so
+ * K's stride_n must be below 2^24 elements there (else SATTN_ERR_UNSUPPORTED). */
 typedef struct {
   void* ptr;
   int B, H, N, d;

@@ -74,6 +74,11 @@ sattn_status check_tensor(const sattn_tensor* t, int B, int H, int N, int d) {
   return SATTN_OK;
 }
 
+// mode 0 reads K rows of a 64-key tile at 32-bit byte offsets row * stride_n * 2
+sattn_status check_k_rows(const sattn_tensor* k, int mode) {
+  return (mode == SATTN_MODE_BF16 && k->stride_n >= (int64_t{1} << 24)) ? SATTN_ERR_UNSUPPORTED : SATTN_OK;
+}
+
 QuantArg quant_arg(const sattn_quant& q) {
   QuantArg a;
   a.B = q.B;
@@ -176,6 +181,7 @@ sattn_status fwd_common(const sattn_tensor* q, const sattn_tensor* k, const satt
   if ((st = check_tensor(v, B, H, Nkv, d)) != SATTN_OK) return st;
   if ((st = check_tensor(o, B, H, Nq, d)) != SATTN_OK) return st;
   if ((st = check_shape(B, H, Nq, Nkv, d, blk_q, blk_k, mode)) != SATTN_OK) return st;
+  if ((st = check_k_rows(k, mode)) != SATTN_OK) return st;
   if (!(std::isfinite(sm_scale))) return SATTN_ERR_INVALID_ARG;
   const Sizes z = sizes(B, H, Nq, Nkv, d, blk_q, mode);
   const size_t need = z.total + scratch_bytes(B, H, Nkv, d, mode);
@@ -258,6 +264,7 @@ sattn_status sattn_fwd_quantized(const sattn_tensor* q, const sattn_tensor* k, c
   if (mode == SATTN_MODE_BF16) {
     if ((st = check_tensor(q, qk->B, qk->H, qk->Nq, qk->d)) != SATTN_OK) return st;
     if ((st = check_tensor(k, qk->B, qk->H, qk->Nkv, qk->d)) != SATTN_OK) return st;
+    if ((st = check_k_rows(k, mode)) != SATTN_OK) return st;
   }
   if (!(std::isfinite(sm_scale))) return SATTN_ERR_INVALID_ARG;
   const float c = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt((float)qk->d);

@@ -1,4 +1,4 @@
-// Fused attention kernels of libsattn for CDNA4 (gfx950).
+// Fused attention kernel of libsattn for CDNA4 (gfx950).
 //
 // One workgroup = 4 waves = 128 query rows of one (batch, head); each wave owns 32 rows.  The workgroup
 // streams 64-key tiles of K and V through LDS and every wave, per tile:
@@ -11,13 +11,15 @@
 //      per-tile scale s_q*s_k*c*log2 e), skipping the O rescale when no running max moved.
 //   3. Round P (bf16, or E4M3 of 448*p) straight into the B operand of the P*V matrix-core op
 //      (v_mfma_f32_32x32x16_bf16 or v_mfma_f32_32x32x64_f8f6f4 reading E4M3), accumulating O^T in fp32.
-// K/V tiles move HBM -> LDS with global_load_lds_dwordx4 (no register staging), two stages, one barrier
-// per tile; the LDS rows are XOR-swizzled in 16-byte granules so that every matrix-operand read is free of
-// bank conflicts.  The score matrix never leaves registers (tutorial "视频生成推理加速实战:从基线到27倍",
-// step 3, item "算子融合与高效注意力"); 8-bit Q*K^T and P*V follow the TMAP I2V write-up (sections
-// "attention量化", "显存优化 / 量化"); the per-call mode is its layer-selective precision (section
-// "保持视频质量").
+// The loop is software-pipelined: the matrix ops of the neighbouring tiles (scores of tile t+1, P*V of tile
+// t-1) are interleaved with the softmax of tile t.  K/V tiles move HBM -> LDS with buffer loads that write LDS
+// directly (no register staging) into a ring of LDS stages, several tiles ahead, one barrier per tile; the LDS
+// rows are XOR-swizzled in 16-byte granules so that every matrix-operand read is free of bank conflicts.  The
+// score matrix never leaves registers (tutorial "视频生成推理加速实战:从基线到27倍", step 3, item
+// "算子融合与高效注意力"); 8-bit Q*K^T and P*V follow the TMAP I2V write-up (sections "attention量化",
+// "显存优化 / 量化"); the per-call mode is its layer-selective precision (section "保持视频质量").
 #include <type_traits>
+#include <utility>
 
 #include "sattn_internal.h"
 
@@ -31,9 +33,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;
-constexpr int kRowsPerWG = kWaves * kRowsPerWave;  // 128
 
 struct AttnArg {
   TensorArg q, k;      // bf16 inputs (mode 0 only)
@@ -41,7 +41,7 @@ struct AttnArg {
   uint16_t* o;
   int64_t osb, osh, osn;
   float clog2e;        // sm_scale * log2(e)
-  int nqt;             // query tiles of 128 rows per (b, h)
+  int nqt;             // query tiles (32 rows per wave of a workgroup) per (b, h)
 };
 
 // Operand row slot i (0..31) of a 32-row block, i = 8a + 4g + t, is fed the element that lands in
@@ -82,13 +82,9 @@ struct Geo {
   static constexpr int KBYTES = kTile * KROW;
   static constexpr int VBYTES = D * VROW;
   static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int KIPW = KBYTES / (16 * 256);  // load instructions per wave for K (4 waves x 64 lanes)
-  static constexpr int VIPW = VBYTES / (16 * 256);
-  static constexpr int IPW = KIPW + VIPW;
   static constexpr int KSTEPS = (MODE == 0) ? D / 16 : D / 32;  // k-steps of the Q*K^T op
   static constexpr int CB = D / 32;                              // 32-channel output blocks
   static constexpr int VREADS = (MODE == 2) ? 2 : 4;             // 16-byte V reads per output block
-  static_assert(KBYTES % (16 * 256) == 0 && VBYTES % (16 * 256) == 0, "tiles split into whole instructions");
   static_assert(2 * STAGE <= 65536, "LDS offsets must fit the 16-bit instruction offset");
 };
 
@@ -101,10 +97,122 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
   return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
 }
 
-template <int MODE, int D>
-__global__ void __launch_bounds__(256, 2) attn_kernel(AttnArg a) {
+// ---------------------------------------------------------------------------------------------------------
+// The software-pipelined key loop.  Iteration t issues, on the matrix cores, P(t-1) V(t-1) and the scores
+// S(t+1) = K(t+1) Q^T, and on the vector ALU the softmax of S(t); the matrix ops are spread through the vector
+// instruction stream, so one wave keeps both units busy.  Tiles stream through an LDS ring (Ring below) whose
+// loads run DIST iterations ahead of their use.
+
+// Raw buffer over one tile (out-of-range loads return zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+// 16 bytes per lane from buffer offset voff into LDS at dst + 16 * lane.
+__device__ __forceinline__ void lds_load16_buf(__amdgpu_buffer_rsrc_t r, int voff, uint8_t* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, voff, 0, 0, 0);
+}
+// 4 bytes per lane from buffer offset voff into LDS at dst + 4 * lane.
+__device__ __forceinline__ void lds_load4_buf(__amdgpu_buffer_rsrc_t r, int voff, uint8_t* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 4, voff, 0, 0, 0);
+}
+// Workgroup barrier of the pipelined loop, without the memory-model waits of __syncthreads (whose workgroup
+// release would wait for every tile load in flight).  Inside the loop LDS is written only by the tile loads,
+// which each wave waits for explicitly (vmcnt) before the barrier, and every LDS read of a stage completes before
+// the barrier that precedes its overwrite; the wavefront-scope fences only stop the compiler from moving LDS
+// accesses across the barrier.
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+// LDS ring of the pipelined kernel with W waves: R stages of one K tile + one V tile (four when the stages fit the
+// 64 KiB that 16-bit LDS instruction offsets reach), loads DIST = R - 1 iterations ahead, one K-scale slot per stage.
+template <int MODE, int D, int W>
+struct Ring {
   using G = Geo<MODE, D>;
+  static constexpr int THREADS = 64 * W;
+  static constexpr int KIPW = G::KBYTES / (16 * THREADS);  // 16-byte-per-lane loads per wave: K tile
+  static constexpr int VIPW = G::VBYTES / (16 * THREADS);  // V tile
+  static constexpr int IPW = KIPW + VIPW;
+  static_assert(KIPW * 16 * THREADS == G::KBYTES && VIPW * 16 * THREADS == G::VBYTES, "tiles split into whole loads");
+  static constexpr int R = (4 * G::STAGE <= 65536) ? 4 : 2;
+  static constexpr int DIST = R - 1;
+  static constexpr int SLOT = 256;          // 64 lanes x 4 B (every lane loads the same scale)
+  static constexpr int OPS = IPW + (MODE != 0);  // loads per wave per iteration (+ the K scale of the 8-bit modes)
+  static constexpr int BYTES = R * G::STAGE + R * SLOT;
+};
+// Waves per workgroup of the pipelined kernel (two per SIMD either way).  Eight waves would share every K/V tile
+// among 256 query rows, but the barrier then couples the two waves of a SIMD and it measured slower than four.
+template <int MODE, int D>
+constexpr int pipe_waves() {
+  return 4;
+}
+// max / sum of a value over lanes n and n + 32 (one v_permlane32_swap)
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Non-template wrappers of the E4M3 builtins (in template-dependent code the host pass would drop the kernel's
+// launch stub).
+__device__ __forceinline__ v16f mfma_e4m3(const v8i& a, const v8i& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+__device__ __forceinline__ int pack_e4m3(float lo0, float lo1, float hi0, float hi1) {
+  const int w = __builtin_amdgcn_cvt_pk_fp8_f32(lo0, lo1, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(hi0, hi1, w, true);
+}
+
+// P of one tile as the B operand of the P*V ops: E4M3 of 448 p (mode 2) or bf16 p (mode 1), keys 32g.. of lane (n, g)
+template <int MODE>
+struct PTile {
+  v8bf b[4];
+};
+template <>
+struct PTile<2> {
+  v8i w;
+};
+
+// Interleaving of one pipelined iteration: LDS operand reads two matrix ops ahead, and after every matrix op a
+// share of the softmax's vector instructions proportional to that op's matrix-core time.
+template <int MODE, int D, bool NEXT>
+struct PipeSchedule {
+  using G = Geo<MODE, D>;
+  static constexpr int NPV = (MODE == 2) ? G::CB : 4 * G::CB;  // P*V ops
+  static constexpr int RPV = (MODE == 2) ? 2 : 1;              // LDS reads per P*V op
+  static constexpr int WPV = (MODE == 2) ? 2 : 1;              // matrix-core time of a P*V op / a Q*K^T op
+  static constexpr int NQK = NEXT ? 2 * G::KSTEPS : 0;
+  static constexpr int NOPS = NPV + NQK;
+  static constexpr int kValu = 176;  // vector instructions of one tile's softmax, about
+  static constexpr int reads(int i) { return i < NPV ? RPV : (i < NOPS ? 1 : 0); }
+  static constexpr int valu(int i) { return kValu * (i < NPV ? WPV : 1) / (NPV * WPV + NQK); }
+  template <int MASK, int N>
+  static __device__ __forceinline__ void group() {
+    // device pass only: a target builtin with template-dependent arguments makes the host pass drop the
+    // kernel's launch stub
+#if defined(__HIP_DEVICE_COMPILE__)
+    if constexpr (N > 0) __builtin_amdgcn_sched_group_barrier(MASK, N, 0);
+#endif
+  }
+  template <int... I>
+  static __device__ __forceinline__ void apply(std::integer_sequence<int, I...>) {
+    group<0x100, reads(0) + reads(1)>();
+    ((group<0x100, reads(I + 2)>(), group<0x008, 1>(), group<0x002, valu(I)>()), ...);
+  }
+  static __device__ __forceinline__ void run() { apply(std::make_integer_sequence<int, NOPS>{}); }
+};
+
+template <int MODE, int D, int W>
+__global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
+  using G = Geo<MODE, D>;
+  using RG = Ring<MODE, D, W>;
+  using SAcc = std::conditional_t<MODE == 0, v16f, v16i>;  // scores: fp32 (bf16 op) or biased int32 (INT8 op)
   constexpr int CB = G::CB;
+  constexpr int KS = G::KSTEPS;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -113,63 +221,55 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(AttnArg a) {
   const int b = logical / (a.nqt * a.qa.H);
   const int64_t bh = (int64_t)b * a.qa.H + h;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int n = lane & 31;  // query of this lane inside the wave's 32 rows
-  const int g = lane >> 5;  // lane half
-  const int q0 = qt * kRowsPerWG + wave * kRowsPerWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: LDS load targets stay scalar
+  const int n = lane & 31;
+  const int g = lane >> 5;
+  const int q0 = qt * (W * kRowsPerWave) + wave * kRowsPerWave;
   const bool active = q0 < a.qa.Nq;
   const int nkb = a.qa.nkb;
   const int Nkv = a.qa.Nkv;
 
-  // ---- per-lane load plan: instruction j of this wave fills LDS granules [(4j + wave) * 64, +64)
-  int ld_off[G::IPW];  // byte offset inside the tile's source (K rows of mode 0: key and column instead)
-  int ld_key[G::KIPW];
+  // ---- per-lane load plan: instruction j of this wave fills LDS granules [(W j + wave) * 64, +64)
+  int ld_off[RG::IPW];
 #pragma unroll
-  for (int j = 0; j < G::IPW; ++j) {
-    const int slot = (4 * j + wave) * 64 + lane;
-    if (j < G::KIPW) {
+  for (int j = 0; j < RG::IPW; ++j) {
+    const int slot = (W * j + wave) * 64 + lane;
+    if (j < RG::KIPW) {
       const int key = slot / G::KG, phys = slot % G::KG;
-      const int col = phys ^ kswz<G::KG>(key);
-      ld_key[j] = key;
-      ld_off[j] = (MODE == 0) ? col * 16 : key * G::KROW + col * 16;
+      const int col = (phys ^ kswz<G::KG>(key)) * 16;
+      ld_off[j] = (MODE == 0) ? key * (int)a.k.sn * 2 + col : key * G::KROW + col;
     } else {
       const int s = slot - G::KBYTES / 16;
       const int ch = s / G::VG, phys = s % G::VG;
-      const int col = phys ^ vswz<G::VG, D>(ch);
-      ld_off[j] = ch * G::VROW + col * 16;
+      ld_off[j] = ch * G::VROW + (phys ^ vswz<G::VG, D>(ch)) * 16;
     }
   }
   const uint8_t* ksrc = (MODE == 0) ? reinterpret_cast<const uint8_t*>(a.k.ptr + b * a.k.sb + h * a.k.sh)
                                     : reinterpret_cast<const uint8_t*>(a.qa.k_codes) + bh * nkb * (int64_t)G::KBYTES;
   const uint8_t* vsrc = ((MODE == 2) ? a.qa.v_codes : reinterpret_cast<const uint8_t*>(a.qa.v_t)) +
                         bh * nkb * (int64_t)G::VBYTES;
-
-  auto issue_tile = [&](int t, int stage) {
-    uint8_t* dst = smem + stage * G::STAGE;
+  auto issue_k = [&](int t, uint8_t* stage) {
+    // mode 0: 64 rows of the bf16 K tensor; the buffer ends after the last row in the sequence, so the rows of a
+    // ragged tile past it read as zero (their scores are masked)
+    const auto r = (MODE == 0) ? tile_rsrc(ksrc + (int64_t)t * kTile * a.k.sn * 2,
+                                           ((min(kTile, Nkv - t * kTile) - 1) * (int)a.k.sn + D) * 2)
+                               : tile_rsrc(ksrc + (int64_t)t * G::KBYTES, G::KBYTES);
 #pragma unroll
-    for (int j = 0; j < G::IPW; ++j) {
-      const uint8_t* src;
-      if (j < G::KIPW) {
-        if (MODE == 0) {
-          const int row = min(t * kTile + ld_key[j], Nkv - 1);  // rows past the sequence are masked later
-          src = ksrc + (int64_t)row * a.k.sn * 2 + ld_off[j];
-        } else {
-          src = ksrc + (int64_t)t * G::KBYTES + ld_off[j];
-        }
-      } else {
-        src = vsrc + (int64_t)t * G::VBYTES + ld_off[j];
-      }
-      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(dst + (4 * j + wave) * 64 * 16), 16, 0, 0);
-    }
+    for (int j = 0; j < RG::KIPW; ++j) lds_load16_buf(r, ld_off[j], stage + (W * j + wave) * 1024);
+  };
+  auto issue_v = [&](int t, uint8_t* stage) {
+    const auto r = tile_rsrc(vsrc + (int64_t)t * G::VBYTES, G::VBYTES);
+#pragma unroll
+    for (int j = RG::KIPW; j < RG::IPW; ++j) lds_load16_buf(r, ld_off[j], stage + (W * j + wave) * 1024);
   };
 
   // ---- per-lane LDS read offsets of the matrix operands (within a stage)
-  int k_rd[2][G::KSTEPS];
+  int k_rd[2][KS];
 #pragma unroll
   for (int bm = 0; bm < 2; ++bm) {
     const int key = slot_key(n, bm);
 #pragma unroll
-    for (int s = 0; s < G::KSTEPS; ++s) k_rd[bm][s] = key * G::KROW + (((2 * s + g) ^ kswz<G::KG>(key)) * 16);
+    for (int s = 0; s < KS; ++s) k_rd[bm][s] = key * G::KROW + (((2 * s + g) ^ kswz<G::KG>(key)) * 16);
   }
   int v_rd[CB][G::VREADS];
 #pragma unroll
@@ -183,14 +283,14 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(AttnArg a) {
   }
 
   // ---- Q fragment (B operand of S^T = K Q^T), resident for the whole key loop
-  v4i qf8[MODE == 0 ? 1 : G::KSTEPS];
-  v8bf qfb[MODE == 0 ? G::KSTEPS : 1];
-  float fq = 0.0f;  // s_q * c * log2(e)
-  if (MODE == 0) {
+  v4i qf8[MODE == 0 ? 1 : KS];
+  v8bf qfb[MODE == 0 ? KS : 1];
+  float fq = 0.0f;  // (s_q *) c * log2(e)
+  if constexpr (MODE == 0) {
     const int row = q0 + n;
     const uint16_t* src = a.q.ptr + b * a.q.sb + h * a.q.sh + (int64_t)row * a.q.sn;
 #pragma unroll
-    for (int s = 0; s < G::KSTEPS; ++s) {
+    for (int s = 0; s < KS; ++s) {
       if (active && row < a.qa.Nq) qfb[s] = *reinterpret_cast<const v8bf*>(src + 16 * s + 8 * g);
       else qfb[s] = (v8bf){};
     }
@@ -199,14 +299,14 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(AttnArg a) {
     if (active) {
       const int8_t* src = a.qa.q_codes + (bh * a.qa.nqb * a.qa.blk_q + q0 + n) * D;
 #pragma unroll
-      for (int s = 0; s < G::KSTEPS; ++s) qf8[s] = *reinterpret_cast<const v4i*>(src + 32 * s + 16 * g);
+      for (int s = 0; s < KS; ++s) qf8[s] = *reinterpret_cast<const v4i*>(src + 32 * s + 16 * g);
       fq = a.qa.q_scales[bh * a.qa.nqb + q0 / a.qa.blk_q] * a.clog2e;
     } else {
 #pragma unroll
-      for (int s = 0; s < G::KSTEPS; ++s) qf8[s] = (v4i){};
+      for (int s = 0; s < KS; ++s) qf8[s] = (v4i){};
     }
   }
-  const float* kscale = a.qa.k_scales + bh * nkb;
+  const float* kscale = (MODE == 0) ? nullptr : a.qa.k_scales + bh * nkb;
 
   v16f oacc[CB];
 #pragma unroll
@@ -214,139 +314,216 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(AttnArg a) {
   float m = -INFINITY;  // running max of x for query n (identical in both lane halves)
   float l = 0.0f;       // this lane's half of the running sum of p (mode 2: of 448 p)
 
-  auto process = [&](const uint8_t* st, int t, auto tail_tag) {
-    constexpr bool TAIL = decltype(tail_tag)::value;
-    const int valid = Nkv - t * kTile;  // keys of this tile inside the sequence (>= 64 unless TAIL)
-    auto in_seq = [&](int bm, int r) { return !TAIL || (32 * g + 16 * bm + r < valid); };
+  // The score accumulators start from the bit pattern of the float 1/(2 pi).  |S| <= 128 * 127^2 keeps the
+  // int32 sum inside that float's binade [1/8, 1/4), so the result read as a float is 1/(2 pi) + S * 2^-26 and
+  // one exact subtraction (Sterbenz) leaves S * 2^-26: cheaper than an int -> float conversion.  Biased values
+  // keep the order of S, so the max runs on the integers.
+  constexpr int kBias = 0x3E22F983;
+  const float bias_f = __int_as_float(kBias);
 
-    // ---------------- 1. scores of 64 keys x 32 queries: two independent accumulation chains
-    float sf[2][16];
-    float smax;
-    if (MODE == 0) {
-      v16f acc[2] = {(v16f){}, (v16f){}};
+  auto qk = [&](const uint8_t* st, SAcc (&acc)[2]) {
+    if constexpr (MODE == 0) {
+      acc[0] = (v16f){};
+      acc[1] = (v16f){};
 #pragma unroll
-      for (int s = 0; s < G::KSTEPS; ++s)
+      for (int s = 0; s < KS; ++s)
 #pragma unroll
         for (int bm = 0; bm < 2; ++bm) {
           const v8bf kv = *reinterpret_cast<const v8bf*>(st + k_rd[bm][s]);
           acc[bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qfb[s], acc[bm], 0, 0, 0);
         }
-      smax = -3.0e38f;
-#pragma unroll
-      for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sf[bm][r] = acc[bm][r];
-          if (in_seq(bm, r)) smax = fmaxf(smax, sf[bm][r]);
-        }
     } else {
-      v16i acc[2] = {(v16i){}, (v16i){}};
+      const v16i bias = {kBias, kBias, kBias, kBias, kBias, kBias, kBias, kBias,
+                         kBias, kBias, kBias, kBias, kBias, kBias, kBias, kBias};
+      acc[0] = bias;
+      acc[1] = bias;
 #pragma unroll
-      for (int s = 0; s < G::KSTEPS; ++s)
+      for (int s = 0; s < KS; ++s)
 #pragma unroll
         for (int bm = 0; bm < 2; ++bm) {
           const v4i kv = *reinterpret_cast<const v4i*>(st + k_rd[bm][s]);
           acc[bm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kv, qf8[s], acc[bm], 0, 0, 0);
         }
-      int imax = -0x7FFFFFFF;
-#pragma unroll
-      for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (in_seq(bm, r)) imax = max(imax, acc[bm][r]);
-#pragma unroll
-      for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sf[bm][r] = (float)acc[bm][r];  // exact: |S| < 2^24
-      smax = (float)imax;  // a half with no key in the sequence gives -2^31, scaled below like the rest
     }
-
-    // ---------------- 2. online softmax (base 2).  x = S*f with f >= 0; rounding is monotone, so the
-    // tile max of x is f times the max of S.  A lane half without keys contributes a value <= 0 that never
-    // exceeds the other half's (for f = 0 every x is 0).
-    const float f = (MODE == 0) ? fq : fq * kscale[t];
-    float xmax = smax * f;
-    xmax = fmaxf(xmax, __shfl_xor(xmax, 32, 64));
-    const float mnew = fmaxf(m, xmax);
-    if (__any(mnew != m)) {
-      const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // 0 on the first tile (m = -inf)
-      l *= alpha;
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
-    }
-    m = mnew;
-    // mode 2 keeps 448 p (= 2^(x - m + log2 448)) so that the E4M3 conversion needs no multiply
-    const float nb = ((MODE == 2) ? 8.807354922057604f : 0.0f) - mnew;
-    float lp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-
-    // ---------------- 3. P rounded into the P*V operand, then P*V
-    if (MODE == 2) {
-      v8i pf;  // E4M3 of 448 p for keys 32g .. 32g+31 (byte j <-> key 32g + j)
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const int bm = w >> 2, r0 = 4 * (w & 3);
-        float p[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sf[bm][r0 + e], f, nb));
-          if (!in_seq(bm, r0 + e)) p[e] = 0.0f;
-          lp[e] += p[e];
-        }
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-        word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
-        pf[w] = word;
-      }
+  };
+  auto pv = [&](const uint8_t* st, const PTile<MODE>& p) {
+    if constexpr (MODE == 2) {
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const v4i lo = *reinterpret_cast<const v4i*>(st + v_rd[cb][0]);
         const v4i hi = *reinterpret_cast<const v4i*>(st + v_rd[cb][1]);
         const v8i vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        oacc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vv, pf, oacc[cb], 0, 0, 0, 0, 0, 0);
+        oacc[cb] = mfma_e4m3(vv, p.w, oacc[cb]);
       }
     } else {
-      v8bf pb[4];  // bf16 p: operand j holds keys 32g + 8j .. 32g + 8j + 7
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int bm = j >> 1, r0 = 8 * (j & 1);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sf[bm][r0 + e], f, nb));
-          if (!in_seq(bm, r0 + e)) p = 0.0f;
-          lp[e & 3] += p;
-          pb[j][e] = (__bf16)p;
-        }
-      }
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const v8bf vv = *reinterpret_cast<const v8bf*>(st + v_rd[cb][j]);
-          oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[j], oacc[cb], 0, 0, 0);
+          oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, p.b[j], oacc[cb], 0, 0, 0);
         }
     }
-    l += (lp[0] + lp[1]) + (lp[2] + lp[3]);
+  };
+  // Online softmax (base 2) of one tile: updates m and l, writes P, returns alpha = 2^(m_old - m_new).
+  // x = S*f with f >= 0; rounding is monotone, so the tile max of x is f times the max of S.  A lane half
+  // without keys in the sequence contributes a value <= 0 that never exceeds the other half's.
+  auto softmax = [&](const SAcc (&acc)[2], float f, int valid, PTile<MODE>& p, auto tail_tag) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    auto in_seq = [&](int bm, int r) { return !TAIL || (32 * g + 16 * bm + r < valid); };
+    // the score of element (bm, r) as a float: S (bf16 op) or S * 2^-26 (unbiased INT8 result)
+    auto score = [&](int bm, int r) {
+      if constexpr (MODE == 0) return acc[bm][r];
+      else return __int_as_float(acc[bm][r]) - bias_f;
+    };
+    float smax;  // tile max of S (in S units); a lane half without keys in the sequence gives a value <= 0
+    if constexpr (MODE == 0) {
+      float fm[4] = {-3.0e38f, -3.0e38f, -3.0e38f, -3.0e38f};
+#pragma unroll
+      for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (in_seq(bm, r)) fm[(2 * bm + r) & 3] = fmaxf(fm[(2 * bm + r) & 3], acc[bm][r]);
+      smax = fmaxf(fmaxf(fm[0], fm[1]), fmaxf(fm[2], fm[3]));
+    } else {
+      int im[4] = {kBias - (1 << 30), kBias - (1 << 30), kBias - (1 << 30), kBias - (1 << 30)};
+#pragma unroll
+      for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (in_seq(bm, r)) im[(2 * bm + r) & 3] = max(im[(2 * bm + r) & 3], acc[bm][r]);
+      smax = (float)(max(max(im[0], im[1]), max(im[2], im[3])) - kBias);
+    }
+    const float xmax = halves_max(smax * f);
+    const float mnew = fmaxf(m, xmax);
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // 0 on the first tile (m = -inf), 1 if m is unchanged
+    const float fe = (MODE == 0) ? f : f * 0x1p26f;         // scale of the stored scores
+    // mode 2 keeps 448 p (= 2^(x - m + log2 448)) so that the E4M3 conversion needs no multiply
+    const float nb = ((MODE == 2) ? 8.807354922057604f : 0.0f) - mnew;
+    float lp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (MODE == 2) {
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const int bm = w >> 2, r0 = 4 * (w & 3);
+        float pe[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(score(bm, r0 + e), fe, nb));
+          if (!in_seq(bm, r0 + e)) pe[e] = 0.0f;
+          lp[e] += pe[e];
+        }
+        p.w[w] = pack_e4m3(pe[0], pe[1], pe[2], pe[3]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int bm = j >> 1, r0 = 8 * (j & 1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(score(bm, r0 + e), fe, nb));
+          if (!in_seq(bm, r0 + e)) pe = 0.0f;
+          lp[e & 3] += pe;
+          p.b[j][e] = (__bf16)pe;
+        }
+      }
+    }
+    l = l * alpha + ((lp[0] + lp[1]) + (lp[2] + lp[3]));
+    m = mnew;
+    return alpha;
   };
 
-  // ---- main loop over the tiles that lie wholly inside the sequence (one barrier per tile; the next
-  // tile's loads fly while this one is computed), then the ragged last tile, if any, on its own path
-  const int nfull = Nkv / kTile;
-  issue_tile(0, 0);
-  for (int t = 0; t < nfull; ++t) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // tile t visible to all waves; everyone is done with the other stage
-    if (t + 1 < nkb) issue_tile(t + 1, (t + 1) & 1);
-    process(smem + (t & 1) * G::STAGE, t, std::false_type{});
+  // ---- LDS ring of R stages.  Iteration t reads stage t % R: K(t+1), V(t-1) and the K block scale of tile
+  // t+1; it loads K(t+1+DIST), V(t-1+DIST) and the scale of tile t+1+DIST into stage (t+DIST) % R, whose last
+  // reader was iteration t-1.  The loads of a stage therefore have DIST iterations to land.
+  constexpr int R = RG::R, DIST = RG::DIST;
+  uint8_t* const slots = smem + R * G::STAGE;  // per-stage K scale slots (RG::SLOT bytes each)
+  auto issue_s = [&](int t, uint8_t* slot) {
+    if constexpr (MODE != 0) lds_load4_buf(tile_rsrc(kscale + t, 4), 0, slot);
+  };
+  auto wait_loads = [&]() {  // every load issued before the last DIST - 1 iterations has landed
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DIST - 1) * RG::OPS) : "memory");
+  };
+
+  // ---- one iteration: P(t-1) V(t-1), S(t+1) (if NEXT) and the softmax of S(t), then the O rescale
+  float ks = 0.0f;  // K block scale of the tile whose softmax comes next
+  auto step = [&](int t, int srd, const SAcc (&scur)[2], SAcc (&snext)[2], const PTile<MODE>& pprev,
+                  PTile<MODE>& pcur, auto tail_tag, auto next_tag) __attribute__((always_inline)) {
+    constexpr bool NEXT = decltype(next_tag)::value;
+    const float f = fq * ks;  // (also completes this wave's read of the scale slot that is reloaded below)
+    wait_loads();
+    ring_barrier();  // stage srd is visible to every wave; every wave is done with stage (srd + DIST) % R
+    const int swr = (srd + DIST) % R;
+    // past the end these reload the last tile, which nothing reads again
+    issue_k(min(t + 1 + DIST, nkb - 1), smem + swr * G::STAGE);
+    issue_v(min(t - 1 + DIST, nkb - 1), smem + swr * G::STAGE);
+    issue_s(min(t + 1 + DIST, nkb - 1), slots + swr * RG::SLOT);
+    const uint8_t* rd = smem + srd * G::STAGE;
+    if constexpr (NEXT && MODE != 0) ks = *reinterpret_cast<const float*>(slots + srd * RG::SLOT);
+    pv(rd, pprev);
+    if constexpr (NEXT) qk(rd, snext);
+    const float mold = m;
+    const float alpha = softmax(scur, f, Nkv - t * kTile, pcur, tail_tag);
+    PipeSchedule<MODE, D, NEXT>::run();
+    // keep P and l computed here, inside the interleaved region, rather than sunk past the rescale branch
+    // (an empty asm reading them; device pass only, its register constraints are the GPU's)
+#if defined(__HIP_DEVICE_COMPILE__)
+    if constexpr (MODE == 2) asm volatile("" ::"v"(pcur.w), "v"(l));
+    else asm volatile("" ::"v"(pcur.b[0]), "v"(pcur.b[1]), "v"(pcur.b[2]), "v"(pcur.b[3]), "v"(l));
+#endif
+    if (__any(m != mold)) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+    }
+  };
+
+  // ---- prologue: stages 0 .. DIST-1 as iterations 0 .. DIST-1 expect them (V of "tile -1" is zeros, read with
+  // P = 0), and K(0) with its scale in stage DIST for the first scores
+#pragma unroll
+  for (int j = 0; j < DIST; ++j) {
+    issue_k(min(j + 1, nkb - 1), smem + j * G::STAGE);
+    if (j > 0) issue_v(min(j - 1, nkb - 1), smem + j * G::STAGE);
+    issue_s(min(j + 1, nkb - 1), slots + j * RG::SLOT);
   }
-  if (nfull < nkb) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    process(smem + (nfull & 1) * G::STAGE, nfull, std::true_type{});
+  issue_k(0, smem + DIST * G::STAGE);
+  issue_s(0, slots + DIST * RG::SLOT);
+  for (int i = threadIdx.x; i < G::VBYTES / 16; i += RG::THREADS)
+    *reinterpret_cast<uint4*>(smem + G::KBYTES + 16 * i) = make_uint4(0, 0, 0, 0);
+  PTile<MODE> pa = {}, pb = {};
+  SAcc sa[2], sb[2];
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  ks = (MODE == 0) ? 1.0f : *reinterpret_cast<const float*>(slots + DIST * RG::SLOT);
+  qk(smem + DIST * G::STAGE, sa);
+
+  // ---- iterations 0 .. nkb-2 have a next tile; groups of R run with constant stage offsets
+  const int nmain = nkb - 1;
+  int t = 0;
+  for (; t + R <= nmain; t += R) {
+    step(t, 0, sa, sb, pa, pb, std::false_type{}, std::true_type{});
+    step(t + 1, 1, sb, sa, pb, pa, std::false_type{}, std::true_type{});
+    if constexpr (R == 4) {
+      step(t + 2, 2, sa, sb, pa, pb, std::false_type{}, std::true_type{});
+      step(t + 3, 3, sb, sa, pb, pa, std::false_type{}, std::true_type{});
+    }
   }
+  for (; t < nmain; ++t) {
+    step(t, t % R, sa, sb, pa, pb, std::false_type{}, std::true_type{});
+    sa[0] = sb[0];
+    sa[1] = sb[1];
+    pa = pb;
+  }
+  // t = nkb - 1: the last tile, ragged or not
+  if (Nkv % kTile) step(t, t % R, sa, sb, pa, pb, std::true_type{}, std::false_type{});
+  else step(t, t % R, sa, sb, pa, pb, std::false_type{}, std::false_type{});
+  wait_loads();
+  ring_barrier();
+  pv(smem + (nkb % R) * G::STAGE, pb);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no tile load may still be writing LDS when the wave exits
 
   // ---------------- epilogue: O = acc / l  (mode 2: acc * s_v[c] / (448 l)), bf16, lane writes D/2 channels
-  const float ltot = l + __shfl_xor(l, 32, 64);
+  const float ltot = halves_sum(l);
   const int row = q0 + n;
   if (!active || row >= a.qa.Nq) return;
   const float inv = 1.0f / ltot;
@@ -370,7 +547,7 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(AttnArg a) {
   }
 }
 
-// Int32 scores of a window, through the same operand layout as attn_kernel (one wave per 32x64 block).
+// Int32 scores of a window, through the same operand layout as attn_pipe_kernel (one wave per 32x64 block).
 template <int D>
 __global__ void __launch_bounds__(64) debug_qk_kernel(QuantArg qa, int64_t bh, int q0, int nq, int k0, int nk,
                                                        int32_t* out) {
@@ -412,17 +589,23 @@ __global__ void __launch_bounds__(64) debug_qk_kernel(QuantArg qa, int64_t bh, i
   }
 }
 
+// bf16 scores (mode 0) run the single-stage loop of 4 waves; the 8-bit modes run the pipelined kernel
 template <int MODE, int D>
-hipError_t launch_attn_t(const AttnArg& a, int nwg, hipStream_t s) {
-  constexpr int bytes = 2 * Geo<MODE, D>::STAGE;
+hipError_t launch_attn_t(AttnArg a, hipStream_t s) {
+  constexpr int W = pipe_waves<MODE, D>();
+  constexpr int bytes = Ring<MODE, D, W>::BYTES;
+  constexpr auto kernel = &attn_pipe_kernel<MODE, D, W>;
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<MODE, D>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       bytes);
     if (e != hipSuccess) return e;
     configured = true;
   }
-  attn_kernel<MODE, D><<<nwg, 256, bytes, s>>>(a);
+  a.nqt = cdiv(a.qa.Nq, W * kRowsPerWave);
+  const int64_t nwg = (int64_t)a.nqt * a.qa.H * a.qa.B;
+  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  kernel<<<(int)nwg, 64 * W, bytes, s>>>(a);
   return hipGetLastError();
 }
 
@@ -439,18 +622,14 @@ hipError_t launch_attn(int mode, const TensorArg& q, const TensorArg& k, const Q
   a.osh = osh;
   a.osn = osn;
   a.clog2e = sm_scale * 1.4426950408889634f;
-  a.nqt = cdiv(qa.Nq, kRowsPerWG);
-  const int64_t nwg64 = (int64_t)a.nqt * qa.H * qa.B;
-  if (nwg64 > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const int nwg = (int)nwg64;
   if (qa.d == 128) {
-    if (mode == 0) return launch_attn_t<0, 128>(a, nwg, s);
-    if (mode == 1) return launch_attn_t<1, 128>(a, nwg, s);
-    return launch_attn_t<2, 128>(a, nwg, s);
+    if (mode == 0) return launch_attn_t<0, 128>(a, s);
+    if (mode == 1) return launch_attn_t<1, 128>(a, s);
+    return launch_attn_t<2, 128>(a, s);
   }
-  if (mode == 0) return launch_attn_t<0, 64>(a, nwg, s);
-  if (mode == 1) return launch_attn_t<1, 64>(a, nwg, s);
-  return launch_attn_t<2, 64>(a, nwg, s);
+  if (mode == 0) return launch_attn_t<0, 64>(a, s);
+  if (mode == 1) return launch_attn_t<1, 64>(a, s);
+  return launch_attn_t<2, 64>(a, s);
 }
 
 hipError_t launch_debug_qk(const QuantArg& qa, int b, int h, int q0, int nq, int k0, int nk, int32_t* out,

@@ -114,6 +114,14 @@ def test_argument_errors_are_caught_on_the_host(S):
     assert fwd(q=_t(S, P, 1, 2, 256, 64, sn=68)) == S.SATTN_ERR_INVALID_ARG  # row stride not a multiple of 8
     bad_d = [_t(S, P, 1, 2, 256, 96) for _ in range(4)]
     assert fwd(*bad_d) == S.SATTN_ERR_UNSUPPORTED
+    # mode 0 addresses K rows with 32-bit offsets: a K row stride of 2^24 elements is refused, 2^24 - 8 is not
+    k_wide = S.sattn_tensor(P, 1, 2, 256, 64, 0, 0, 1 << 24)
+    k_ok = S.sattn_tensor(P, 1, 2, 256, 64, 0, 0, (1 << 24) - 8)
+    ws0 = S.sattn_workspace_bytes(1, 2, 256, 256, 64, 64, 64, 0)
+    assert fwd(k=k_wide, mode=0, ws_bytes=ws0) == S.SATTN_ERR_UNSUPPORTED
+    assert fwd(k=k_ok, mode=0, ws_bytes=ws0, ws=P + 16) == S.SATTN_ERR_INVALID_ARG  # (passes the stride check)
+    assert fwd(k=k_wide, mode=2, ws=P + 16) == S.SATTN_ERR_INVALID_ARG  # the limit is mode 0's; mode 2 gets
+    # past it to the (misaligned) workspace check
     # cross-attention and the quantized entry points validate the same way
     assert L.sattn_cross_fwd(byref(q), byref(k), byref(v), byref(o), 0.0, 2, None, 0, None) == S.SATTN_ERR_WORKSPACE
     assert L.sattn_fwd_quantized(None, None, None, byref(o), 0.0, 2, None) == S.SATTN_ERR_INVALID_ARG
