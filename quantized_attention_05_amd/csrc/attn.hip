@@ -19,7 +19,6 @@
 // "算子融合与高效注意力"); 8-bit Q*K^T and P*V follow the TMAP I2V write-up (sections "attention量化",
 // "显存优化 / 量化"); the per-call mode is its layer-selective precision (section "保持视频质量").
 #include <type_traits>
-#include <utility>
 
 #include "sattn_internal.h"
 
@@ -177,35 +176,6 @@ struct PTile<2> {
   v8i w;
 };
 
-// Interleaving of one pipelined iteration: LDS operand reads two matrix ops ahead, and after every matrix op a
-// share of the softmax's vector instructions proportional to that op's matrix-core time.
-template <int MODE, int D, bool NEXT>
-struct PipeSchedule {
-  using G = Geo<MODE, D>;
-  static constexpr int NPV = (MODE == 2) ? G::CB : 4 * G::CB;  // P*V ops
-  static constexpr int RPV = (MODE == 2) ? 2 : 1;              // LDS reads per P*V op
-  static constexpr int WPV = (MODE == 2) ? 2 : 1;              // matrix-core time of a P*V op / a Q*K^T op
-  static constexpr int NQK = NEXT ? 2 * G::KSTEPS : 0;
-  static constexpr int NOPS = NPV + NQK;
-  static constexpr int kValu = 176;  // vector instructions of one tile's softmax, about
-  static constexpr int reads(int i) { return i < NPV ? RPV : (i < NOPS ? 1 : 0); }
-  static constexpr int valu(int i) { return kValu * (i < NPV ? WPV : 1) / (NPV * WPV + NQK); }
-  template <int MASK, int N>
-  static __device__ __forceinline__ void group() {
-    // device pass only: a target builtin with template-dependent arguments makes the host pass drop the
-    // kernel's launch stub
-#if defined(__HIP_DEVICE_COMPILE__)
-    if constexpr (N > 0) __builtin_amdgcn_sched_group_barrier(MASK, N, 0);
-#endif
-  }
-  template <int... I>
-  static __device__ __forceinline__ void apply(std::integer_sequence<int, I...>) {
-    group<0x100, reads(0) + reads(1)>();
-    ((group<0x100, reads(I + 2)>(), group<0x008, 1>(), group<0x002, valu(I)>()), ...);
-  }
-  static __device__ __forceinline__ void run() { apply(std::make_integer_sequence<int, NOPS>{}); }
-};
-
 template <int MODE, int D, int W>
 __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
   using G = Geo<MODE, D>;
@@ -321,6 +291,13 @@ __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
   constexpr int kBias = 0x3E22F983;
   const float bias_f = __int_as_float(kBias);
 
+  // INT8 modes: the bias block lives in registers for the whole loop (the empty asm hides that it is a constant,
+  // so the compiler feeds it to the first matrix op of each tile instead of rebuilding it every tile)
+  v16i bias_acc = {kBias, kBias, kBias, kBias, kBias, kBias, kBias, kBias,
+                   kBias, kBias, kBias, kBias, kBias, kBias, kBias, kBias};
+#if defined(__HIP_DEVICE_COMPILE__)
+  if constexpr (MODE != 0) asm volatile("" : "+v"(bias_acc));
+#endif
   auto qk = [&](const uint8_t* st, SAcc (&acc)[2]) {
     if constexpr (MODE == 0) {
       acc[0] = (v16f){};
@@ -333,10 +310,8 @@ __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
           acc[bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qfb[s], acc[bm], 0, 0, 0);
         }
     } else {
-      const v16i bias = {kBias, kBias, kBias, kBias, kBias, kBias, kBias, kBias,
-                         kBias, kBias, kBias, kBias, kBias, kBias, kBias, kBias};
-      acc[0] = bias;
-      acc[1] = bias;
+      acc[0] = bias_acc;
+      acc[1] = bias_acc;
 #pragma unroll
       for (int s = 0; s < KS; ++s)
 #pragma unroll
@@ -463,9 +438,10 @@ __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
     if constexpr (NEXT) qk(rd, snext);
     const float mold = m;
     const float alpha = softmax(scur, f, Nkv - t * kTile, pcur, tail_tag);
-    PipeSchedule<MODE, D, NEXT>::run();
-    // keep P and l computed here, inside the interleaved region, rather than sunk past the rescale branch
-    // (an empty asm reading them; device pass only, its register constraints are the GPU's)
+    // Keep P and l computed here, in the same scheduling region as the matrix ops above, rather than sunk past
+    // the rescale branch (an empty asm reading them; device pass only, its register constraints are the GPU's).
+    // Within the region the compiler's own scheduler interleaves the matrix ops with the softmax; explicit
+    // scheduling groups measured slower.
 #if defined(__HIP_DEVICE_COMPILE__)
     if constexpr (MODE == 2) asm volatile("" ::"v"(pcur.w), "v"(l));
     else asm volatile("" ::"v"(pcur.b[0]), "v"(pcur.b[1]), "v"(pcur.b[2]), "v"(pcur.b[3]), "v"(l));
