@@ -72,6 +72,11 @@ def lib() -> ctypes.CDLL:
         L.orc_attn_emulate.restype = None
         L.orc_attn_ref_fp64.argtypes = [i32, i32, f64, P, P, P, P, i32, P]
         L.orc_attn_ref_fp64.restype = None
+        L.orc_attn_emulate_masked.argtypes = [i32, i32, i32, i32, i32, i32, f32, P, P, P, P, P, P, P, P, P, P, i32,
+                                              P, i32, P, P]
+        L.orc_attn_emulate_masked.restype = None
+        L.orc_attn_ref_fp64_masked.argtypes = [i32, i32, f64, P, P, P, P, i32, P, i32, P]
+        L.orc_attn_ref_fp64_masked.restype = None
         L.orc_max_threads.argtypes, L.orc_max_threads.restype = [], i32
         _lib = L
     return _lib
@@ -179,13 +184,27 @@ def qk_int(q_codes: np.ndarray, k_codes: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- attention
+MASK_KBLK = 64  # keys per block of a block-sparse mask
+
+
+def _mask_arg(mask, rows, nkv: int, mask_qblk: int):
+    """A [query blocks, key blocks] byte mask checked against the rows and keys it must cover."""
+    m = np.ascontiguousarray(np.asarray(mask) != 0, dtype=np.uint8)
+    nkb = -(-nkv // MASK_KBLK)
+    assert m.ndim == 2 and m.shape[1] == nkb, (m.shape, nkb)
+    assert rows.size == 0 or m.shape[0] > int(rows.max()) // mask_qblk
+    return m
+
+
 def attn_emulate(mode: int, rows, *, tile: int, sm_scale: float, blk_q: int, blk_k: int, nkv: int,
-                 q_bf16=None, k_bf16=None, v_bf16=None, quant: dict | None = None, want_f32: bool = False):
+                 q_bf16=None, k_bf16=None, v_bf16=None, quant: dict | None = None, want_f32: bool = False,
+                 mask=None, mask_qblk: int = 128):
     """Tile-faithful replay of the quantized attention for the given query rows of one head slice.
 
     mode 0 needs q_bf16, k_bf16, v_bf16; mode 1 needs quant (q/k codes and scales) and v_bf16;
     mode 2 needs quant including v_codes/v_scales.  Returns bf16 bit patterns [len(rows), d]
-    (and the fp32 values before the final rounding if want_f32).
+    (and the fp32 values before the final rounding if want_f32).  With mask ([ceil(rows/mask_qblk),
+    ceil(nkv/64)], nonzero = keep), only the kept key blocks of a row's query block take part.
     """
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
     qb = kb = vb = qc = qs = kc = ks = vc = vs = None
@@ -206,17 +225,30 @@ def attn_emulate(mode: int, rows, *, tile: int, sm_scale: float, blk_q: int, blk
             assert vc.shape[0] >= nkv
     out = np.empty((rows.size, d), dtype=np.uint16)
     of = np.empty((rows.size, d), dtype=np.float32) if want_f32 else None
-    lib().orc_attn_emulate(mode, nkv, d, blk_q, blk_k, tile, float(sm_scale), _ptr(qb), _ptr(kb), _ptr(qc), _ptr(qs),
-                           _ptr(kc), _ptr(ks), _ptr(vb), _ptr(vc), _ptr(vs), _ptr(rows), rows.size, _ptr(out), _ptr(of))
+    if mask is None:
+        lib().orc_attn_emulate(mode, nkv, d, blk_q, blk_k, tile, float(sm_scale), _ptr(qb), _ptr(kb), _ptr(qc),
+                               _ptr(qs), _ptr(kc), _ptr(ks), _ptr(vb), _ptr(vc), _ptr(vs), _ptr(rows), rows.size,
+                               _ptr(out), _ptr(of))
+    else:
+        m = _mask_arg(mask, rows, nkv, mask_qblk)
+        lib().orc_attn_emulate_masked(mode, nkv, d, blk_q, blk_k, tile, float(sm_scale), _ptr(qb), _ptr(kb), _ptr(qc),
+                                      _ptr(qs), _ptr(kc), _ptr(ks), _ptr(vb), _ptr(vc), _ptr(vs), _ptr(rows),
+                                      rows.size, _ptr(m), mask_qblk, _ptr(out), _ptr(of))
     return (out, of) if want_f32 else out
 
 
-def attn_ref_fp64(q_bf16, k_bf16, v_bf16, rows, sm_scale: float) -> np.ndarray:
-    """Exact attention softmax(c*q*K^T)*V in fp64 for the given rows of one head slice."""
+def attn_ref_fp64(q_bf16, k_bf16, v_bf16, rows, sm_scale: float, mask=None, mask_qblk: int = 128) -> np.ndarray:
+    """Exact attention softmax(c*q*K^T)*V in fp64 for the given rows of one head slice (with mask: over the
+    keys of the kept key blocks; a row with none gives 0)."""
     qb, kb, vb = _dense(q_bf16, np.uint16), _dense(k_bf16, np.uint16), _dense(v_bf16, np.uint16)
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
     d = qb.shape[1]
     out = np.empty((rows.size, d), dtype=np.float64)
-    lib().orc_attn_ref_fp64(kb.shape[0], d, float(sm_scale), _ptr(qb), _ptr(kb), _ptr(vb), _ptr(rows), rows.size,
-                            _ptr(out))
+    if mask is None:
+        lib().orc_attn_ref_fp64(kb.shape[0], d, float(sm_scale), _ptr(qb), _ptr(kb), _ptr(vb), _ptr(rows), rows.size,
+                                _ptr(out))
+    else:
+        m = _mask_arg(mask, rows, kb.shape[0], mask_qblk)
+        lib().orc_attn_ref_fp64_masked(kb.shape[0], d, float(sm_scale), _ptr(qb), _ptr(kb), _ptr(vb), _ptr(rows),
+                                       rows.size, _ptr(m), mask_qblk, _ptr(out))
     return out

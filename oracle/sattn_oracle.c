@@ -17,6 +17,9 @@
  *   - Attention precision is switched per layer (section "保持视频质量"): the three modes below.
  *   - The score matrix is never materialised; softmax is computed online over key tiles (page
  *     "视频生成推理加速实战:从基线到27倍", step 3 "引擎级优化", item "算子融合与高效注意力").
+ *   - Block-sparse attention computes only the regions a sparse block mask selects (page
+ *     "视频生成模型的高效推理加速机制解析", section "核心组成与关键能力", item 3 "稀疏注意力", and step 3 of
+ *     "工作原理与执行流程").
  * The pages give no formulas for the quantizer; the readings taken here (K smoothing by its per-channel
  * mean, symmetric per-block INT8 with scale amax/127, per-channel E4M3 for V with scale amax/448, the
  * guard threshold 2^-100, P quantized relative to the running max) are the plainest ones consistent with
@@ -217,12 +220,22 @@ void orc_qk_int(const int8_t* qc, int nq, const int8_t* kc, int nk, int d, int64
 /* Row r uses Q block r/blk_q; key j uses K block j/blk_k.  Only `rows` (nrows indices) are computed. */
 /* All matrices dense row-major: q_bf16/k_bf16/v_bf16 [n, d] bf16; q_codes [.., d]; k_codes [.., d];  */
 /* v_codes [nkv, d].  out: bf16 [nrows, d]; out_f32 (may be NULL): [nrows, d] fp32 before rounding.   */
+/*                                                                                                   */
+/* Block-sparse variant (page "视频生成模型的高效推理加速机制解析", section "核心组成与关键能力", item 3, and */
+/* step 3 of "工作原理与执行流程": the attention layer computes only the regions its sparse mask selects):  */
+/* keep, when not NULL, is a [ceil(rows/mask_qblk), nkb] byte mask over query blocks of mask_qblk rows and */
+/* key blocks of ORC_MASK_KBLK keys (nkb = ceil(nkv / ORC_MASK_KBLK)); key j counts for row r only if     */
+/* keep[(r / mask_qblk) * nkb + j / ORC_MASK_KBLK] != 0.  Keys that do not count are left out of every    */
+/* step (the running max, l and acc); a tile without such keys changes nothing; a row with none gets 0.  */
 /* ------------------------------------------------------------------------------------------------ */
-void orc_attn_emulate(int mode, int nkv, int d, int blk_q, int blk_k, int tile, float sm_scale,
-                      const uint16_t* q_bf16, const uint16_t* k_bf16, const int8_t* q_codes,
-                      const float* q_scales, const int8_t* k_codes, const float* k_scales,
-                      const uint16_t* v_bf16, const uint8_t* v_codes, const float* v_scales,
-                      const int* rows, int nrows, uint16_t* out, float* out_f32) {
+#define ORC_MASK_KBLK 64
+void orc_attn_emulate_masked(int mode, int nkv, int d, int blk_q, int blk_k, int tile, float sm_scale,
+                             const uint16_t* q_bf16, const uint16_t* k_bf16, const int8_t* q_codes,
+                             const float* q_scales, const int8_t* k_codes, const float* k_scales,
+                             const uint16_t* v_bf16, const uint8_t* v_codes, const float* v_scales,
+                             const int* rows, int nrows, const uint8_t* keep, int mask_qblk, uint16_t* out,
+                             float* out_f32) {
+  const int nkb = (nkv + ORC_MASK_KBLK - 1) / ORC_MASK_KBLK;
   const float clog2e = sm_scale * 1.4426950408889634f; /* c * log2(e) in fp32 */
   /* V^ as numbers: the bf16 values (modes 0/1) or the decoded E4M3 codes (mode 2) */
   float* vhat = (float*)malloc(sizeof(float) * (size_t)nkv * d);
@@ -247,11 +260,16 @@ void orc_attn_emulate(int mode, int nkv, int d, int blk_q, int blk_k, int tile, 
       float m = -INFINITY;
       double l = 0.0;
       for (int c = 0; c < d; ++c) acc[c] = 0.0;
+      const uint8_t* keep_row = keep ? keep + (long long)(r / mask_qblk) * nkb : NULL;
       for (int j0 = 0; j0 < nkv; j0 += tile) {
         const int j1 = (j0 + tile) < nkv ? (j0 + tile) : nkv;
-        /* step 7: dequantized, pre-scaled logits of this tile */
+        /* step 7: dequantized, pre-scaled logits of this tile (keys left out by the mask: x = -inf) */
         float tmax = -INFINITY;
         for (int j = j0; j < j1; ++j) {
+          if (keep_row && !keep_row[j / ORC_MASK_KBLK]) {
+            x[j - j0] = -INFINITY;
+            continue;
+          }
           float xv;
           if (mode == 0) {
             double s = 0.0;
@@ -266,12 +284,14 @@ void orc_attn_emulate(int mode, int nkv, int d, int blk_q, int blk_k, int tile, 
           x[j - j0] = xv;
           if (xv > tmax) tmax = xv;
         }
+        if (tmax == -INFINITY) continue; /* no key of this tile counts for this row */
         /* step 8: online softmax update */
         const float mnew = tmax > m ? tmax : m;
         const double alpha = (m == -INFINITY) ? 0.0 : (double)(float)exp2((double)m - (double)mnew);
         double psum = 0.0;
         for (int c = 0; c < d; ++c) acc[c] *= alpha;
         for (int j = j0; j < j1; ++j) {
+          if (x[j - j0] == -INFINITY) continue;
           const float p = (float)exp2((double)x[j - j0] - (double)mnew);
           psum += (double)p;
           const double ph = (mode == 2) ? (double)orc_e4m3_decode(orc_e4m3_encode(p * 448.0f))
@@ -282,9 +302,9 @@ void orc_attn_emulate(int mode, int nkv, int d, int blk_q, int blk_k, int tile, 
         l = alpha * l + psum;
         m = mnew;
       }
-      /* step 9: epilogue */
+      /* step 9: epilogue (a row whose mask keeps no key: O = 0) */
       for (int c = 0; c < d; ++c) {
-        double o = (mode == 2) ? acc[c] * (double)v_scales[c] / (448.0 * l) : acc[c] / l;
+        double o = (l == 0.0) ? 0.0 : (mode == 2) ? acc[c] * (double)v_scales[c] / (448.0 * l) : acc[c] / l;
         float of = (float)o;
         if (out_f32) out_f32[(long long)ri * d + c] = of;
         out[(long long)ri * d + c] = orc_bf16_from_f32(of);
@@ -298,12 +318,24 @@ void orc_attn_emulate(int mode, int nkv, int d, int blk_q, int blk_k, int tile, 
   free(kf);
 }
 
+void orc_attn_emulate(int mode, int nkv, int d, int blk_q, int blk_k, int tile, float sm_scale,
+                      const uint16_t* q_bf16, const uint16_t* k_bf16, const int8_t* q_codes,
+                      const float* q_scales, const int8_t* k_codes, const float* k_scales,
+                      const uint16_t* v_bf16, const uint8_t* v_codes, const float* v_scales,
+                      const int* rows, int nrows, uint16_t* out, float* out_f32) {
+  orc_attn_emulate_masked(mode, nkv, d, blk_q, blk_k, tile, sm_scale, q_bf16, k_bf16, q_codes, q_scales, k_codes,
+                          k_scales, v_bf16, v_codes, v_scales, rows, nrows, NULL, 1, out, out_f32);
+}
+
 /* ------------------------------------------------------------------------------------------------ */
 /* Exact attention in fp64 from the bf16 inputs: O = softmax(c * q * K^T) * V, the operator that the  */
-/* quantized modes approximate.  out: fp64 [nrows, d].                                               */
+/* quantized modes approximate.  out: fp64 [nrows, d].  With keep (as in orc_attn_emulate_masked),    */
+/* the softmax runs over the keys the mask keeps for the row; a row with none gets 0.                 */
 /* ------------------------------------------------------------------------------------------------ */
-void orc_attn_ref_fp64(int nkv, int d, double sm_scale, const uint16_t* q_bf16, const uint16_t* k_bf16,
-                       const uint16_t* v_bf16, const int* rows, int nrows, double* out) {
+void orc_attn_ref_fp64_masked(int nkv, int d, double sm_scale, const uint16_t* q_bf16, const uint16_t* k_bf16,
+                              const uint16_t* v_bf16, const int* rows, int nrows, const uint8_t* keep,
+                              int mask_qblk, double* out) {
+  const int nkb = (nkv + ORC_MASK_KBLK - 1) / ORC_MASK_KBLK;
   double* kd = (double*)malloc(sizeof(double) * (size_t)nkv * d);
   double* vd = (double*)malloc(sizeof(double) * (size_t)nkv * d);
   for (long long i = 0; i < (long long)nkv * d; ++i) {
@@ -319,8 +351,13 @@ void orc_attn_ref_fp64(int nkv, int d, double sm_scale, const uint16_t* q_bf16, 
     for (int ri = 0; ri < nrows; ++ri) {
       const int r = rows[ri];
       for (int c = 0; c < d; ++c) qd[c] = orc_bf16_to_f32(q_bf16[(long long)r * d + c]);
+      const uint8_t* keep_row = keep ? keep + (long long)(r / mask_qblk) * nkb : NULL;
       double mx = -INFINITY;
       for (int j = 0; j < nkv; ++j) {
+        if (keep_row && !keep_row[j / ORC_MASK_KBLK]) {
+          s[j] = -INFINITY;
+          continue;
+        }
         double dot = 0.0;
         for (int c = 0; c < d; ++c) dot += qd[c] * kd[(long long)j * d + c];
         s[j] = sm_scale * dot;
@@ -329,11 +366,12 @@ void orc_attn_ref_fp64(int nkv, int d, double sm_scale, const uint16_t* q_bf16, 
       double den = 0.0;
       for (int c = 0; c < d; ++c) num[c] = 0.0;
       for (int j = 0; j < nkv; ++j) {
+        if (s[j] == -INFINITY) continue;
         const double w = exp(s[j] - mx);
         den += w;
         for (int c = 0; c < d; ++c) num[c] += w * vd[(long long)j * d + c];
       }
-      for (int c = 0; c < d; ++c) out[(long long)ri * d + c] = num[c] / den;
+      for (int c = 0; c < d; ++c) out[(long long)ri * d + c] = (den == 0.0) ? 0.0 : num[c] / den;
     }
     free(s);
     free(qd);
@@ -341,6 +379,11 @@ void orc_attn_ref_fp64(int nkv, int d, double sm_scale, const uint16_t* q_bf16, 
   }
   free(kd);
   free(vd);
+}
+
+void orc_attn_ref_fp64(int nkv, int d, double sm_scale, const uint16_t* q_bf16, const uint16_t* k_bf16,
+                       const uint16_t* v_bf16, const int* rows, int nrows, double* out) {
+  orc_attn_ref_fp64_masked(nkv, d, sm_scale, q_bf16, k_bf16, v_bf16, rows, nrows, NULL, 1, out);
 }
 
 int orc_max_threads(void) {
