@@ -106,6 +106,62 @@ def layer_selective(args):
     }), flush=True)
 
 
+def block_sparse(args):
+    """Block-sparse self-attention at the Wan-14B 720p shape (INT8+FP8 unless --mode says otherwise) with a local
+    band mask (query block i keeps the key blocks within 9450 tokens of it, plus the first block: ~24 % of the
+    blocks).  Reports the TOPS of the work actually done (kept query-key pairs) and, for comparison, the dense call
+    on the same inputs.  Inputs are drawn on the GPU (values do not change the timing)."""
+    import torch
+
+    from quantized_attention_05_amd import sattn
+    from quantized_attention_05_amd import workloads as wl
+
+    w = wl.WORKLOADS["wan14b-720p"]
+    mode = args.mode
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(w.seed)
+    shape = (w.B, w.H, w.Nq, w.d)
+    q, k, v = (torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16) for _ in range(3))
+    mask_np = wl.band_block_mask(w, half_width=9450)
+    mask = torch.from_numpy(mask_np).to(dev)
+    pairs = wl.kept_pairs(w, mask_np)
+    ops_kept = 4.0 * pairs * w.d
+    o = torch.empty_like(q)
+    ws = torch.empty(sattn.sattn_workspace_bytes(w.B, w.H, w.Nq, w.Nkv, w.d, w.blk_q, 64, mode), dtype=torch.uint8,
+                     device=dev)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms = timed(lambda: sattn.fwd_block_sparse(q, k, v, mask, mode=mode, sm_scale=w.sm_scale, blk_q=w.blk_q, out=o,
+                                              workspace=ws))
+    ms_dense = timed(lambda: sattn.fwd(q, k, v, mode=mode, sm_scale=w.sm_scale, blk_q=w.blk_q, out=o, workspace=ws))
+    print(json.dumps({
+        "metric": "block-sparse attention TOPS on the kept blocks, Wan-14B 720p self-attn, local band mask",
+        "value": round(ops_kept / (ms * 1e-3) / 1e12, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": MODE_DTYPE[mode],
+        "data": "synthetic: N(0,1) drawn on the GPU; band block mask (recipe in DESIGN.md)",
+        "config": {"workload": "wan14b-720p block-sparse self-attention", "B": w.B, "H": w.H, "Nq": w.Nq,
+                   "Nkv": w.Nkv, "d": w.d, "mode": wl.MODE_NAMES[mode], "mask": "band, half-width 9450 tokens, 1 sink",
+                   "kept_block_fraction": round(float(mask_np.mean()), 4),
+                   "kept_pair_fraction": round(pairs / (w.B * w.H * w.Nq * w.Nkv), 4)},
+        "dense_ms_per_step": round(ms_dense, 3),
+        "speedup_vs_dense": round(ms_dense / ms, 3),
+        "dense_equivalent_tops": round(w.ops / (ms * 1e-3) / 1e12, 2),
+    }), flush=True)
+
+
 def cpu_baseline(w, mode: int, budget_s: float):
     """The oracle, as it stands, on a bounded sample: quantize one head in full, then emulate query blocks of
     that head until about `budget_s` seconds of CPU time are spent.  Extrapolated linearly to the whole call
@@ -155,7 +211,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan14b-720p",
-                    help="a name from quantized_attention_05_amd.workloads.WORKLOADS, or 'layersel'")
+                    help="a name from quantized_attention_05_amd.workloads.WORKLOADS, 'layersel' or 'sparse'")
     ap.add_argument("--mode", type=int, default=2, choices=[0, 1, 2])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -181,6 +237,9 @@ def main():
         sys.exit(2)
     if args.workload == "layersel":
         layer_selective(args)
+        return
+    if args.workload == "sparse":
+        block_sparse(args)
         return
 
     import torch

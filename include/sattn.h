@@ -152,6 +152,20 @@ sattn_status sattn_cross_fwd(const sattn_tensor* q, const sattn_tensor* k, const
                              const sattn_tensor* o, float sm_scale, int mode, void* ws, size_t ws_bytes,
                              sattn_stream_t stream);
 
+/* Block-sparse self-attention: the attention layer computes only the regions a sparse block mask selects
+ * (page "视频生成模型的高效推理加速机制解析", section "核心组成与关键能力", item 3 "稀疏注意力", and step 3 of
+ * "工作原理与执行流程").  As sattn_fwd, except that the query rows of mask block i (rows SATTN_MASK_QBLK*i ..
+ * SATTN_MASK_QBLK*(i+1)-1) attend only to the keys of the key blocks j (keys SATTN_MASK_KBLK*j ..) with
+ *   block_mask[((b*H + h)*nqm + i)*nkm + j] != 0,   nqm = ceil(Nq / SATTN_MASK_QBLK), nkm = ceil(Nkv / SATTN_MASK_KBLK).
+ * Keys left out take no part in the softmax; query rows whose mask row keeps nothing get O = 0.  Quantization
+ * (K mean, scales) still uses every key.  block_mask: device bytes, read only, B*H*nqm*nkm of them.
+ * Errors: SATTN_ERR_INVALID_ARG for a NULL mask, SATTN_ERR_UNSUPPORTED for nkm > 32768, else as sattn_fwd. */
+#define SATTN_MASK_QBLK 128
+#define SATTN_MASK_KBLK 64
+sattn_status sattn_fwd_block_sparse(const sattn_tensor* q, const sattn_tensor* k, const sattn_tensor* v,
+                                    const sattn_tensor* o, const uint8_t* block_mask, float sm_scale, int mode,
+                                    int blk_q, int blk_k, void* ws, size_t ws_bytes, sattn_stream_t stream);
+
 /* Test hook: the int32 scores S = q_codes . k_codes^T of one (b, h) for query rows [q0, q0+nq) and keys
  * [k0, k0+nk), computed with the same INT8 matrix-core path as the attention kernel.
  * out: device int32 [nq, nk] row-major.  Rows/keys must lie inside the padded code arrays. */

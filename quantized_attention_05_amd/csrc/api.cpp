@@ -171,7 +171,8 @@ sattn_status layout(int B, int H, int Nq, int Nkv, int d, int blk_q, int blk_k, 
 }
 
 sattn_status fwd_common(const sattn_tensor* q, const sattn_tensor* k, const sattn_tensor* v, const sattn_tensor* o,
-                        float sm_scale, int mode, int blk_q, int blk_k, void* ws, size_t ws_bytes, hipStream_t s) {
+                        float sm_scale, int mode, int blk_q, int blk_k, void* ws, size_t ws_bytes,
+                        const uint8_t* mask, hipStream_t s) {
   if (!q || !k || !v || !o) return SATTN_ERR_INVALID_ARG;
   const int B = q->B, H = q->H, Nq = q->N, Nkv = k->N, d = q->d;
   sattn_status st;
@@ -195,7 +196,7 @@ sattn_status fwd_common(const sattn_tensor* q, const sattn_tensor* k, const satt
   const float c = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt((float)d);
   const TensorArg ot = tensor_arg(o);
   return hip_status(launch_attn(mode, tensor_arg(q), tensor_arg(k), quant_arg(qk), const_cast<uint16_t*>(ot.ptr), ot.sb,
-                                ot.sh, ot.sn, c, s));
+                                ot.sh, ot.sn, c, mask, s));
 }
 
 }  // namespace
@@ -273,19 +274,29 @@ sattn_status sattn_fwd_quantized(const sattn_tensor* q, const sattn_tensor* k, c
   const TensorArg qt = mode == SATTN_MODE_BF16 ? tensor_arg(q) : none;
   const TensorArg kt = mode == SATTN_MODE_BF16 ? tensor_arg(k) : none;
   return hip_status(launch_attn(mode, qt, kt, quant_arg(*qk), const_cast<uint16_t*>(ot.ptr), ot.sb, ot.sh, ot.sn, c,
-                                reinterpret_cast<hipStream_t>(stream)));
+                                nullptr, reinterpret_cast<hipStream_t>(stream)));
 }
 
 sattn_status sattn_fwd(const sattn_tensor* q, const sattn_tensor* k, const sattn_tensor* v, const sattn_tensor* o,
                        float sm_scale, int mode, int blk_q, int blk_k, void* ws, size_t ws_bytes,
                        sattn_stream_t stream) {
-  return fwd_common(q, k, v, o, sm_scale, mode, blk_q, blk_k, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+  return fwd_common(q, k, v, o, sm_scale, mode, blk_q, blk_k, ws, ws_bytes, nullptr,
+                    reinterpret_cast<hipStream_t>(stream));
+}
+
+sattn_status sattn_fwd_block_sparse(const sattn_tensor* q, const sattn_tensor* k, const sattn_tensor* v,
+                                    const sattn_tensor* o, const uint8_t* block_mask, float sm_scale, int mode,
+                                    int blk_q, int blk_k, void* ws, size_t ws_bytes, sattn_stream_t stream) {
+  if (!block_mask || !k) return SATTN_ERR_INVALID_ARG;
+  if (k->N > 0 && cdiv(k->N, SATTN_MASK_KBLK) > kMaxSparseTiles) return SATTN_ERR_UNSUPPORTED;
+  return fwd_common(q, k, v, o, sm_scale, mode, blk_q, blk_k, ws, ws_bytes, block_mask,
+                    reinterpret_cast<hipStream_t>(stream));
 }
 
 sattn_status sattn_cross_fwd(const sattn_tensor* q, const sattn_tensor* k, const sattn_tensor* v,
                              const sattn_tensor* o, float sm_scale, int mode, void* ws, size_t ws_bytes,
                              sattn_stream_t stream) {
-  return fwd_common(q, k, v, o, sm_scale, mode, 128, kTile, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+  return fwd_common(q, k, v, o, sm_scale, mode, 128, kTile, ws, ws_bytes, nullptr, reinterpret_cast<hipStream_t>(stream));
 }
 
 sattn_status sattn_debug_qk_int32(const sattn_quant* qk, int b, int h, int q0, int nq, int k0, int nk, int32_t* out,

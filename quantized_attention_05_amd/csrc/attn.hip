@@ -41,6 +41,7 @@ struct AttnArg {
   int64_t osb, osh, osn;
   float clog2e;        // sm_scale * log2(e)
   int nqt;             // query tiles (32 rows per wave of a workgroup) per (b, h)
+  const uint8_t* mask; // block-sparse: [B, H, nqt, nkb] bytes, nonzero = attend to that key tile (else unused)
 };
 
 // Operand row slot i (0..31) of a 32-row block, i = 8a + 4g + t, is fed the element that lands in
@@ -139,6 +140,10 @@ struct Ring {
   static constexpr int SLOT = 256;          // 64 lanes x 4 B (every lane loads the same scale)
   static constexpr int OPS = IPW + (MODE != 0);  // loads per wave per iteration (+ the K scale of the 8-bit modes)
   static constexpr int BYTES = R * G::STAGE + R * SLOT;
+  // block-sparse: after the ring, the count of kept key tiles (16 bytes) and their indices (uint16 each)
+  static constexpr int LIST_OFF = BYTES;
+  static constexpr int MAX_LIST = kMaxSparseTiles;
+  static constexpr int SPARSE_BYTES = BYTES + 16 + ((2 * MAX_LIST + 15) / 16) * 16;
 };
 // Waves per workgroup of the pipelined kernel (two per SIMD either way).  Eight waves would share every K/V tile
 // among 256 query rows, but the barrier then couples the two waves of a SIMD and it measured slower than four.
@@ -176,10 +181,11 @@ struct PTile<2> {
   v8i w;
 };
 
-template <int MODE, int D, int W>
+template <int MODE, int D, int W, bool SPARSE>
 __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
   using G = Geo<MODE, D>;
   using RG = Ring<MODE, D, W>;
+  static_assert(!SPARSE || W * kRowsPerWave == kMaskQRows, "one mask row per workgroup query tile");
   using SAcc = std::conditional_t<MODE == 0, v16f, v16i>;  // scores: fp32 (bf16 op) or biased int32 (INT8 op)
   constexpr int CB = G::CB;
   constexpr int KS = G::KSTEPS;
@@ -407,9 +413,44 @@ __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
     return alpha;
   };
 
-  // ---- LDS ring of R stages.  Iteration t reads stage t % R: K(t+1), V(t-1) and the K block scale of tile
-  // t+1; it loads K(t+1+DIST), V(t-1+DIST) and the scale of tile t+1+DIST into stage (t+DIST) % R, whose last
-  // reader was iteration t-1.  The loads of a stage therefore have DIST iterations to land.
+  // ---- the key tiles this workgroup attends to, in ascending order: all nkb of them, or (block-sparse) the tiles
+  // its mask row keeps, listed in LDS by wave 0.  Iteration i of the loop below handles tile tile_of(i).
+  int ntile = nkb;
+  const uint16_t* list = reinterpret_cast<const uint16_t*>(smem + RG::LIST_OFF + 16);
+  if constexpr (SPARSE) {
+    if (wave == 0) {
+      uint16_t* wlist = reinterpret_cast<uint16_t*>(smem + RG::LIST_OFF + 16);
+      const uint8_t* mrow = a.mask + ((int64_t)bh * a.nqt + qt) * nkb;
+      int cnt = 0;
+      for (int base = 0; base < nkb; base += 64) {
+        const int j = base + lane;
+        const bool keep = j < nkb && mrow[j] != 0;
+        const uint64_t bal = __ballot(keep);
+        if (keep) wlist[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (uint16_t)j;
+        cnt += __popcll(bal);
+      }
+      if (lane == 0) *reinterpret_cast<int*>(smem + RG::LIST_OFF) = cnt;
+    }
+    __syncthreads();
+    ntile = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(smem + RG::LIST_OFF));
+    if (ntile == 0) {  // nothing to attend to: O = 0 (uniform over the workgroup, no load in flight)
+      const int row = q0 + n;
+      if (active && row < a.qa.Nq) {
+        uint4* dst = reinterpret_cast<uint4*>(a.o + b * a.osb + h * a.osh + (int64_t)row * a.osn + (D / 2) * g);
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) dst[i] = make_uint4(0, 0, 0, 0);
+      }
+      return;
+    }
+  }
+  auto tile_of = [&](int i) -> int {
+    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane(list[i]);
+    else return i;
+  };
+
+  // ---- LDS ring of R stages.  Iteration i reads stage i % R: K and the K block scale of tile_of(i+1) and V of
+  // tile_of(i-1); it loads K and the scale of tile_of(i+1+DIST) and V of tile_of(i-1+DIST) into stage
+  // (i+DIST) % R, whose last reader was iteration i-1.  The loads of a stage therefore have DIST iterations to land.
   constexpr int R = RG::R, DIST = RG::DIST;
   uint8_t* const slots = smem + R * G::STAGE;  // per-stage K scale slots (RG::SLOT bytes each)
   auto issue_s = [&](int t, uint8_t* slot) {
@@ -419,9 +460,10 @@ __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DIST - 1) * RG::OPS) : "memory");
   };
 
-  // ---- one iteration: P(t-1) V(t-1), S(t+1) (if NEXT) and the softmax of S(t), then the O rescale
+  // ---- one iteration: P V of the previous tile, S of the next one (if NEXT) and the softmax of this one, then
+  // the O rescale
   float ks = 0.0f;  // K block scale of the tile whose softmax comes next
-  auto step = [&](int t, int srd, const SAcc (&scur)[2], SAcc (&snext)[2], const PTile<MODE>& pprev,
+  auto step = [&](int i, int srd, const SAcc (&scur)[2], SAcc (&snext)[2], const PTile<MODE>& pprev,
                   PTile<MODE>& pcur, auto tail_tag, auto next_tag) __attribute__((always_inline)) {
     constexpr bool NEXT = decltype(next_tag)::value;
     const float f = fq * ks;  // (also completes this wave's read of the scale slot that is reloaded below)
@@ -429,15 +471,15 @@ __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
     ring_barrier();  // stage srd is visible to every wave; every wave is done with stage (srd + DIST) % R
     const int swr = (srd + DIST) % R;
     // past the end these reload the last tile, which nothing reads again
-    issue_k(min(t + 1 + DIST, nkb - 1), smem + swr * G::STAGE);
-    issue_v(min(t - 1 + DIST, nkb - 1), smem + swr * G::STAGE);
-    issue_s(min(t + 1 + DIST, nkb - 1), slots + swr * RG::SLOT);
+    issue_k(tile_of(min(i + 1 + DIST, ntile - 1)), smem + swr * G::STAGE);
+    issue_v(tile_of(min(i - 1 + DIST, ntile - 1)), smem + swr * G::STAGE);
+    issue_s(tile_of(min(i + 1 + DIST, ntile - 1)), slots + swr * RG::SLOT);
     const uint8_t* rd = smem + srd * G::STAGE;
     if constexpr (NEXT && MODE != 0) ks = *reinterpret_cast<const float*>(slots + srd * RG::SLOT);
     pv(rd, pprev);
     if constexpr (NEXT) qk(rd, snext);
     const float mold = m;
-    const float alpha = softmax(scur, f, Nkv - t * kTile, pcur, tail_tag);
+    const float alpha = softmax(scur, f, Nkv - tile_of(i) * kTile, pcur, tail_tag);
     // Keep P and l computed here, in the same scheduling region as the matrix ops above, rather than sunk past
     // the rescale branch (an empty asm reading them; device pass only, its register constraints are the GPU's).
     // Within the region the compiler's own scheduler interleaves the matrix ops with the softmax; explicit
@@ -455,15 +497,15 @@ __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
   };
 
   // ---- prologue: stages 0 .. DIST-1 as iterations 0 .. DIST-1 expect them (V of "tile -1" is zeros, read with
-  // P = 0), and K(0) with its scale in stage DIST for the first scores
+  // P = 0), and K of the first tile with its scale in stage DIST for the first scores
 #pragma unroll
   for (int j = 0; j < DIST; ++j) {
-    issue_k(min(j + 1, nkb - 1), smem + j * G::STAGE);
-    if (j > 0) issue_v(min(j - 1, nkb - 1), smem + j * G::STAGE);
-    issue_s(min(j + 1, nkb - 1), slots + j * RG::SLOT);
+    issue_k(tile_of(min(j + 1, ntile - 1)), smem + j * G::STAGE);
+    if (j > 0) issue_v(tile_of(min(j - 1, ntile - 1)), smem + j * G::STAGE);
+    issue_s(tile_of(min(j + 1, ntile - 1)), slots + j * RG::SLOT);
   }
-  issue_k(0, smem + DIST * G::STAGE);
-  issue_s(0, slots + DIST * RG::SLOT);
+  issue_k(tile_of(0), smem + DIST * G::STAGE);
+  issue_s(tile_of(0), slots + DIST * RG::SLOT);
   for (int i = threadIdx.x; i < G::VBYTES / 16; i += RG::THREADS)
     *reinterpret_cast<uint4*>(smem + G::KBYTES + 16 * i) = make_uint4(0, 0, 0, 0);
   PTile<MODE> pa = {}, pb = {};
@@ -473,29 +515,29 @@ __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
   ks = (MODE == 0) ? 1.0f : *reinterpret_cast<const float*>(slots + DIST * RG::SLOT);
   qk(smem + DIST * G::STAGE, sa);
 
-  // ---- iterations 0 .. nkb-2 have a next tile; groups of R run with constant stage offsets
-  const int nmain = nkb - 1;
-  int t = 0;
-  for (; t + R <= nmain; t += R) {
-    step(t, 0, sa, sb, pa, pb, std::false_type{}, std::true_type{});
-    step(t + 1, 1, sb, sa, pb, pa, std::false_type{}, std::true_type{});
+  // ---- iterations 0 .. ntile-2 have a next tile; groups of R run with constant stage offsets
+  const int nmain = ntile - 1;
+  int i = 0;
+  for (; i + R <= nmain; i += R) {
+    step(i, 0, sa, sb, pa, pb, std::false_type{}, std::true_type{});
+    step(i + 1, 1, sb, sa, pb, pa, std::false_type{}, std::true_type{});
     if constexpr (R == 4) {
-      step(t + 2, 2, sa, sb, pa, pb, std::false_type{}, std::true_type{});
-      step(t + 3, 3, sb, sa, pb, pa, std::false_type{}, std::true_type{});
+      step(i + 2, 2, sa, sb, pa, pb, std::false_type{}, std::true_type{});
+      step(i + 3, 3, sb, sa, pb, pa, std::false_type{}, std::true_type{});
     }
   }
-  for (; t < nmain; ++t) {
-    step(t, t % R, sa, sb, pa, pb, std::false_type{}, std::true_type{});
+  for (; i < nmain; ++i) {
+    step(i, i % R, sa, sb, pa, pb, std::false_type{}, std::true_type{});
     sa[0] = sb[0];
     sa[1] = sb[1];
     pa = pb;
   }
-  // t = nkb - 1: the last tile, ragged or not
-  if (Nkv % kTile) step(t, t % R, sa, sb, pa, pb, std::true_type{}, std::false_type{});
-  else step(t, t % R, sa, sb, pa, pb, std::false_type{}, std::false_type{});
+  // i = ntile - 1: the last tile; only the sequence's last tile can be ragged
+  if (Nkv % kTile && tile_of(i) == nkb - 1) step(i, i % R, sa, sb, pa, pb, std::true_type{}, std::false_type{});
+  else step(i, i % R, sa, sb, pa, pb, std::false_type{}, std::false_type{});
   wait_loads();
   ring_barrier();
-  pv(smem + (nkb % R) * G::STAGE, pb);
+  pv(smem + (ntile % R) * G::STAGE, pb);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no tile load may still be writing LDS when the wave exits
 
   // ---------------- epilogue: O = acc / l  (mode 2: acc * s_v[c] / (448 l)), bf16, lane writes D/2 channels
@@ -565,18 +607,20 @@ __global__ void __launch_bounds__(64) debug_qk_kernel(QuantArg qa, int64_t bh, i
   }
 }
 
-// bf16 scores (mode 0) run the single-stage loop of 4 waves; the 8-bit modes run the pipelined kernel
 template <int MODE, int D>
 hipError_t launch_attn_t(AttnArg a, hipStream_t s) {
   constexpr int W = pipe_waves<MODE, D>();
-  constexpr int bytes = Ring<MODE, D, W>::BYTES;
-  constexpr auto kernel = &attn_pipe_kernel<MODE, D, W>;
-  static bool configured = false;
-  if (!configured) {
+  using RG = Ring<MODE, D, W>;
+  const bool sparse = a.mask != nullptr;
+  const auto kernel = sparse ? &attn_pipe_kernel<MODE, D, W, true> : &attn_pipe_kernel<MODE, D, W, false>;
+  // dense: the ring; block-sparse: the ring + the tile list (sized for this call's key tiles)
+  const int bytes = sparse ? RG::LIST_OFF + 16 + cdiv(2 * a.qa.nkb, 16) * 16 : RG::BYTES;
+  static bool configured[2] = {false, false};
+  if (!configured[sparse]) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       bytes);
+                                       sparse ? RG::SPARSE_BYTES : RG::BYTES);
     if (e != hipSuccess) return e;
-    configured = true;
+    configured[sparse] = true;
   }
   a.nqt = cdiv(a.qa.Nq, W * kRowsPerWave);
   const int64_t nwg = (int64_t)a.nqt * a.qa.H * a.qa.B;
@@ -588,7 +632,7 @@ hipError_t launch_attn_t(AttnArg a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attn(int mode, const TensorArg& q, const TensorArg& k, const QuantArg& qa, uint16_t* o, int64_t osb,
-                       int64_t osh, int64_t osn, float sm_scale, hipStream_t s) {
+                       int64_t osh, int64_t osn, float sm_scale, const uint8_t* mask, hipStream_t s) {
   AttnArg a;
   a.q = q;
   a.k = k;
@@ -598,6 +642,7 @@ hipError_t launch_attn(int mode, const TensorArg& q, const TensorArg& k, const Q
   a.osh = osh;
   a.osn = osn;
   a.clog2e = sm_scale * 1.4426950408889634f;
+  a.mask = mask;
   if (qa.d == 128) {
     if (mode == 0) return launch_attn_t<0, 128>(a, s);
     if (mode == 1) return launch_attn_t<1, 128>(a, s);

@@ -11,6 +11,8 @@ namespace sattn {
 constexpr int kTile = 64;          // keys per softmax tile == K quantization block == V tile
 constexpr int kChunk = 64;         // tokens per run of the K-mean / V-amax first pass
 constexpr float kGuard = 0x1p-100f; // amax below this: all-zero block or channel (scale 0, codes 0)
+constexpr int kMaskQRows = SATTN_MASK_QBLK;  // block-sparse mask: query rows per mask row
+constexpr int kMaxSparseTiles = 32768;       // block-sparse: key tiles per mask row the kernel can list in LDS
 
 inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
@@ -45,8 +47,9 @@ hipError_t launch_kv_finalize(const QuantArg& qa, bool with_v, const float* ksum
                               hipStream_t s);
 hipError_t launch_kv_quant(const TensorArg& k, const TensorArg& v, int mode, const QuantArg& qa, const float* vinv,
                            hipStream_t s);
+// mask: nullptr for dense attention, else the block-sparse mask [B, H, ceil(Nq/128), ceil(Nkv/64)] (device bytes)
 hipError_t launch_attn(int mode, const TensorArg& q, const TensorArg& k, const QuantArg& qa, uint16_t* o, int64_t osb,
-                       int64_t osh, int64_t osn, float sm_scale, hipStream_t s);
+                       int64_t osh, int64_t osn, float sm_scale, const uint8_t* mask, hipStream_t s);
 hipError_t launch_debug_qk(const QuantArg& qa, int b, int h, int q0, int nq, int k0, int nk, int32_t* out,
                            hipStream_t s);
 

@@ -64,6 +64,7 @@ SYMBOLS = [
     ("sattn_fwd_quantized", _I, [_TP, _TP, _QP, _TP, ctypes.c_float, _I, _P]),
     ("sattn_fwd", _I, [_TP, _TP, _TP, _TP, ctypes.c_float, _I, _I, _I, _P, _SZ, _P]),
     ("sattn_cross_fwd", _I, [_TP, _TP, _TP, _TP, ctypes.c_float, _I, _P, _SZ, _P]),
+    ("sattn_fwd_block_sparse", _I, [_TP, _TP, _TP, _TP, _P, ctypes.c_float, _I, _I, _I, _P, _SZ, _P]),
     ("sattn_debug_qk_int32", _I, [_QP, _I, _I, _I, _I, _I, _I, _P, _P]),
 ]
 
@@ -134,6 +135,13 @@ def sattn_cross_fwd(q, k, v, o, sm_scale, mode, ws: int, ws_bytes: int, stream: 
                                  ws_bytes, ctypes.c_void_p(stream)), "sattn_cross_fwd")
 
 
+def sattn_fwd_block_sparse(q, k, v, o, block_mask: int, sm_scale, mode, blk_q, blk_k, ws: int, ws_bytes: int,
+                           stream: int):
+    _check(lib().sattn_fwd_block_sparse(_ref(q), _ref(k), _ref(v), _ref(o), ctypes.c_void_p(block_mask),
+                                        float(sm_scale), mode, blk_q, blk_k, ctypes.c_void_p(ws), ws_bytes,
+                                        ctypes.c_void_p(stream)), "sattn_fwd_block_sparse")
+
+
 def sattn_debug_qk_int32(qk: sattn_quant, b, h, q0, nq, k0, nk, out: int, stream: int):
     _check(lib().sattn_debug_qk_int32(ctypes.byref(qk), b, h, q0, nq, k0, nk, ctypes.c_void_p(out),
                                       ctypes.c_void_p(stream)), "sattn_debug_qk_int32")
@@ -173,6 +181,35 @@ def fwd(q, k, v, mode=SATTN_MODE_I8_FP8, sm_scale=None, blk_q=128, blk_k=64, out
     ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=q.device)
     sattn_fwd(tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(o), _resolve(sm_scale, d), mode, blk_q, blk_k,
               ws.data_ptr(), ws.numel(), _stream())
+    return o
+
+
+MASK_QBLK = 128  # query rows per block-sparse mask row (SATTN_MASK_QBLK)
+MASK_KBLK = 64   # keys per block-sparse mask column (SATTN_MASK_KBLK)
+
+
+def mask_shape(B, H, Nq, Nkv):
+    """Shape of the block-sparse mask of sattn_fwd_block_sparse: [B, H, ceil(Nq/128), ceil(Nkv/64)]."""
+    return (B, H, -(-Nq // MASK_QBLK), -(-Nkv // MASK_KBLK))
+
+
+def fwd_block_sparse(q, k, v, mask, mode=SATTN_MODE_I8_FP8, sm_scale=None, blk_q=128, blk_k=64, out=None,
+                     workspace=None):
+    """Block-sparse self-attention through sattn_fwd_block_sparse.  mask: uint8 (nonzero = keep) on the GPU, shaped
+    mask_shape(B, H, Nq, Nkv), contiguous.  Returns O like q."""
+    B, H, Nq, d = q.shape
+    Nkv = k.shape[2]
+    if tuple(mask.shape) != mask_shape(B, H, Nq, Nkv) or mask.dtype != torch.uint8 or not mask.is_contiguous():
+        raise SattnError(SATTN_ERR_INVALID_ARG, "fwd_block_sparse: mask shape/dtype/layout")
+    if mask.device != q.device:
+        raise SattnError(SATTN_ERR_INVALID_ARG, "fwd_block_sparse: mask must be on the GPU of q")
+    o = torch.empty_like(q) if out is None else out
+    need = sattn_workspace_bytes(B, H, Nq, Nkv, d, blk_q, blk_k, mode)
+    if need == 0:
+        raise SattnError(SATTN_ERR_UNSUPPORTED, "sattn_workspace_bytes")
+    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=q.device)
+    sattn_fwd_block_sparse(tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(o), mask.data_ptr(),
+                           _resolve(sm_scale, d), mode, blk_q, blk_k, ws.data_ptr(), ws.numel(), _stream())
     return o
 
 

@@ -139,3 +139,38 @@ def bits(t: torch.Tensor) -> np.ndarray:
 def scaled(w: Workload, **changes) -> Workload:
     """The same recipe at other sizes (for tests that need a smaller instance of a workload)."""
     return dataclasses.replace(w, **changes)
+
+
+# ---------------------------------------------------------------- block-sparse masks
+# A block mask is [B, H, ceil(Nq / 128), ceil(Nkv / 64)] bytes: 1 = query block i attends to key block j.
+MASK_QBLK = 128
+MASK_KBLK = 64
+
+
+def mask_dims(w: Workload) -> Tuple[int, int, int, int]:
+    return (w.B, w.H, -(-w.Nq // MASK_QBLK), -(-w.Nkv // MASK_KBLK))
+
+
+def random_block_mask(w: Workload, density: float, seed: int) -> np.ndarray:
+    """Each block kept independently with probability ``density`` (PCG64 stream of ``seed``)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return (rng.random(mask_dims(w)) < density).astype(np.uint8)
+
+
+def band_block_mask(w: Workload, half_width: int, sink_blocks: int = 1) -> np.ndarray:
+    """Local attention: query block i keeps key block j when their token centres lie within ``half_width`` tokens,
+    plus the first ``sink_blocks`` key blocks; the same pattern for every (batch, head)."""
+    B, H, nqm, nkm = mask_dims(w)
+    qc = np.arange(nqm) * MASK_QBLK + MASK_QBLK // 2
+    kc = np.arange(nkm) * MASK_KBLK + MASK_KBLK // 2
+    keep = np.abs(qc[:, None] - kc[None, :]) <= half_width
+    keep[:, :sink_blocks] = True
+    return np.ascontiguousarray(np.broadcast_to(keep, (B, H, nqm, nkm)).astype(np.uint8))
+
+
+def kept_pairs(w: Workload, mask: np.ndarray) -> int:
+    """(query, key) pairs a block mask keeps, counting the ragged last blocks at their true sizes."""
+    B, H, nqm, nkm = mask_dims(w)
+    rq = np.minimum(MASK_QBLK, w.Nq - np.arange(nqm) * MASK_QBLK)
+    rk = np.minimum(MASK_KBLK, w.Nkv - np.arange(nkm) * MASK_KBLK)
+    return int(np.einsum("bhij,i,j->", (np.asarray(mask) != 0).astype(np.int64), rq, rk))

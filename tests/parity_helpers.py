@@ -72,17 +72,20 @@ def oracle_quant(w: wl.Workload, b: int, h: int, mode: int, blk_q: int, seed=Non
     return oracle.quantize_head(q, k, v, blk_q, 64, mode)
 
 
-def oracle_outputs(w: wl.Workload, b: int, h: int, mode: int, rows, blk_q: int, sm_scale: float, seed=None):
-    """(E as fp32 values of its bf16 output, R in fp64) for the given rows of one head."""
+def oracle_outputs(w: wl.Workload, b: int, h: int, mode: int, rows, blk_q: int, sm_scale: float, seed=None,
+                   mask=None):
+    """(E as fp32 values of its bf16 output, R in fp64) for the given rows of one head (with a block-sparse
+    mask: the [query blocks, key blocks] mask of this head)."""
     q, k, v = head_bits(w, b, h, seed)
+    mk = {} if mask is None else {"mask": mask, "mask_qblk": wl.MASK_QBLK}
     if mode == 0:
         E = oracle.attn_emulate(0, rows, tile=64, sm_scale=sm_scale, blk_q=blk_q, blk_k=64, nkv=w.Nkv,
-                                q_bf16=q, k_bf16=k, v_bf16=v)
+                                q_bf16=q, k_bf16=k, v_bf16=v, **mk)
     else:
         qz = oracle.quantize_head(q, k, v, blk_q, 64, mode)
         E = oracle.attn_emulate(mode, rows, tile=64, sm_scale=sm_scale, blk_q=blk_q, blk_k=64, nkv=w.Nkv,
-                                quant=qz, v_bf16=v)
-    R = oracle.attn_ref_fp64(q, k, v, rows, sm_scale)
+                                quant=qz, v_bf16=v, **mk)
+    R = oracle.attn_ref_fp64(q, k, v, rows, sm_scale, **mk)
     return f32(E).astype(np.float64), R
 
 

@@ -122,6 +122,16 @@ def test_argument_errors_are_caught_on_the_host(S):
     assert fwd(k=k_ok, mode=0, ws_bytes=ws0, ws=P + 16) == S.SATTN_ERR_INVALID_ARG  # (passes the stride check)
     assert fwd(k=k_wide, mode=2, ws=P + 16) == S.SATTN_ERR_INVALID_ARG  # the limit is mode 0's; mode 2 gets
     # past it to the (misaligned) workspace check
+    # block-sparse: the mask is required, at most 32768 key blocks, otherwise it validates like sattn_fwd
+    mk = ctypes.c_void_p(P)
+    def sparse(k=k, mask=mk, ws=P):
+        return L.sattn_fwd_block_sparse(byref(q), byref(k), byref(v), byref(o), mask, 0.0, 2, 64, 64,
+                                        ctypes.c_void_p(ws), ws_need, None)
+    assert sparse(mask=None) == S.SATTN_ERR_INVALID_ARG
+    k_long = _t(S, P, 1, 2, 32768 * 64 + 1, 64)
+    assert sparse(k=k_long) == S.SATTN_ERR_UNSUPPORTED
+    assert sparse(ws=P + 16) == S.SATTN_ERR_INVALID_ARG            # reaches the workspace check
+    assert sparse(k=_t(S, P, 1, 2, 200, 64), ws=P + 16) == S.SATTN_ERR_INVALID_ARG  # K rows != V rows
     # cross-attention and the quantized entry points validate the same way
     assert L.sattn_cross_fwd(byref(q), byref(k), byref(v), byref(o), 0.0, 2, None, 0, None) == S.SATTN_ERR_WORKSPACE
     assert L.sattn_fwd_quantized(None, None, None, byref(o), 0.0, 2, None) == S.SATTN_ERR_INVALID_ARG
