@@ -162,6 +162,55 @@ def block_sparse(args):
     }), flush=True)
 
 
+def layer_probe(args):
+    """The per-layer attention-error probe of layer-selective quantization at the Wan-14B 720p layer shape: the
+    layer's self-attention in mode 2 and in mode 0 on the same inputs, then the per-head error sums on the GPU.
+    Reports the time of one layer's probe and, separately, of the error-sum kernel (which reads both outputs)."""
+    import torch
+
+    from quantized_attention_05_amd import policy
+    from quantized_attention_05_amd import sattn
+    from quantized_attention_05_amd import workloads as wl
+
+    w = wl.WORKLOADS["wan14b-720p"]
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(w.seed)
+    shape = (w.B, w.H, w.Nq, w.d)
+    q, k, v = (torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16) for _ in range(3))
+    ws = torch.empty(max(sattn.sattn_workspace_bytes(w.B, w.H, w.Nq, w.Nkv, w.d, w.blk_q, 64, m) for m in (0, 2)),
+                     dtype=torch.uint8, device=dev)
+    o2 = sattn.fwd(q, k, v, mode=2, sm_scale=w.sm_scale, workspace=ws)
+    o0 = sattn.fwd(q, k, v, mode=0, sm_scale=w.sm_scale, workspace=ws)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(args.warmup):
+        sattn.error_stats(o2, o0)
+    e0.record(stream)
+    for _ in range(args.steps):
+        sattn.error_stats(o2, o0)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    stats_ms = e0.elapsed_time(e1) / args.steps
+    for _ in range(args.warmup):
+        policy.probe_error(q, k, v, mode=2, sm_scale=w.sm_scale, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        rel, cos, _ = policy.probe_error(q, k, v, mode=2, sm_scale=w.sm_scale, workspace=ws)
+    probe_ms = (time.perf_counter() - t0) * 1e3 / args.steps  # includes the host copy of the 40 x 4 sums
+    out_bytes = 2 * w.B * w.H * w.Nq * w.d * 2
+    print(json.dumps({
+        "metric": "per-layer attention-error probe time (mode 2 vs bf16 + per-head error sums), Wan-14B 720p layer",
+        "value": round(probe_ms, 3), "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(probe_ms, 3), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8+fp8e4m3 vs bf16; sums in f64", "data": "synthetic: N(0,1) drawn on the GPU",
+        "config": {"workload": "wan14b-720p layer probe", "B": w.B, "H": w.H, "N": w.Nq, "d": w.d},
+        "error_stats_ms": round(stats_ms, 4),
+        "error_stats_gbps": round(out_bytes / (stats_ms * 1e-3) / 1e9, 1),
+        "rel_l2_mode2_vs_bf16": rel, "cos_mode2_vs_bf16": cos,
+    }), flush=True)
+
+
 def cpu_baseline(w, mode: int, budget_s: float):
     """The oracle, as it stands, on a bounded sample: quantize one head in full, then emulate query blocks of
     that head until about `budget_s` seconds of CPU time are spent.  Extrapolated linearly to the whole call
@@ -211,7 +260,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan14b-720p",
-                    help="a name from quantized_attention_05_amd.workloads.WORKLOADS, 'layersel' or 'sparse'")
+                    help="a name from quantized_attention_05_amd.workloads.WORKLOADS, 'layersel', 'sparse' or 'probe'")
     ap.add_argument("--mode", type=int, default=2, choices=[0, 1, 2])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -240,6 +289,9 @@ def main():
         return
     if args.workload == "sparse":
         block_sparse(args)
+        return
+    if args.workload == "probe":
+        layer_probe(args)
         return
 
     import torch

@@ -166,6 +166,16 @@ sattn_status sattn_fwd_block_sparse(const sattn_tensor* q, const sattn_tensor* k
                                     const sattn_tensor* o, const uint8_t* block_mask, float sm_scale, int mode,
                                     int blk_q, int blk_k, void* ws, size_t ws_bytes, sattn_stream_t stream);
 
+/* Attention-error probe of layer-selective quantization (TMAP I2V write-up, section "保持视频质量": the error of each
+ * attention layer over the denoising iterations, against the original precision, decides which layers keep it).
+ * For two outputs a and ref of the same shape [B,H,N,d] (bf16, e.g. a quantized-mode call and the mode-0 call on the
+ * same inputs), writes per (b, h) the fp64 sums over rows and channels
+ *   out[(b*H + h)*4 + 0..3] = sum (a - ref)^2, sum ref^2, sum a*ref, sum a^2
+ * (relative L2 error = sqrt(out0 / out1), cosine = out2 / sqrt(out1 * out3)).  out: device memory, 8-byte aligned,
+ * B*H*4 doubles.  Deterministic (fixed summation order); allocates nothing.  Errors: SATTN_ERR_INVALID_ARG for
+ * NULL or mismatched tensors, SATTN_ERR_UNSUPPORTED for d outside {64, 128} or B*H > 65535. */
+sattn_status sattn_error_stats(const sattn_tensor* a, const sattn_tensor* ref, double* out, sattn_stream_t stream);
+
 /* Test hook: the int32 scores S = q_codes . k_codes^T of one (b, h) for query rows [q0, q0+nq) and keys
  * [k0, k0+nk), computed with the same INT8 matrix-core path as the attention kernel.
  * out: device int32 [nq, nk] row-major.  Rows/keys must lie inside the padded code arrays. */

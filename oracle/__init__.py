@@ -252,3 +252,14 @@ def attn_ref_fp64(q_bf16, k_bf16, v_bf16, rows, sm_scale: float, mask=None, mask
         lib().orc_attn_ref_fp64_masked(kb.shape[0], d, float(sm_scale), _ptr(qb), _ptr(kb), _ptr(vb), _ptr(rows),
                                        rows.size, _ptr(m), mask_qblk, _ptr(out))
     return out
+
+
+# ---------------------------------------------------------------- per-layer error probe
+def error_stats(a_bits, r_bits) -> np.ndarray:
+    """The probe's sums for one head slice, by definition, in fp64: [sum (a-r)^2, sum r^2, sum a*r, sum a^2] over all
+    elements of two bf16 arrays (16-bit patterns) of equal shape."""
+    a = (np.asarray(a_bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    r = (np.asarray(r_bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert a.shape == r.shape
+    d = a - r
+    return np.array([np.sum(d * d), np.sum(r * r), np.sum(a * r), np.sum(a * a)])

@@ -50,6 +50,8 @@ hipError_t launch_kv_quant(const TensorArg& k, const TensorArg& v, int mode, con
 // mask: nullptr for dense attention, else the block-sparse mask [B, H, ceil(Nq/128), ceil(Nkv/64)] (device bytes)
 hipError_t launch_attn(int mode, const TensorArg& q, const TensorArg& k, const QuantArg& qa, uint16_t* o, int64_t osb,
                        int64_t osh, int64_t osn, float sm_scale, const uint8_t* mask, hipStream_t s);
+hipError_t launch_error_stats(const TensorArg& a, const TensorArg& r, int B, int H, int N, int d, double* out,
+                              hipStream_t s);
 hipError_t launch_debug_qk(const QuantArg& qa, int b, int h, int q0, int nq, int k0, int nk, int32_t* out,
                            hipStream_t s);
 

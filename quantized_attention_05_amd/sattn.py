@@ -65,6 +65,7 @@ SYMBOLS = [
     ("sattn_fwd", _I, [_TP, _TP, _TP, _TP, ctypes.c_float, _I, _I, _I, _P, _SZ, _P]),
     ("sattn_cross_fwd", _I, [_TP, _TP, _TP, _TP, ctypes.c_float, _I, _P, _SZ, _P]),
     ("sattn_fwd_block_sparse", _I, [_TP, _TP, _TP, _TP, _P, ctypes.c_float, _I, _I, _I, _P, _SZ, _P]),
+    ("sattn_error_stats", _I, [_TP, _TP, _P, _P]),
     ("sattn_debug_qk_int32", _I, [_QP, _I, _I, _I, _I, _I, _I, _P, _P]),
 ]
 
@@ -140,6 +141,11 @@ def sattn_fwd_block_sparse(q, k, v, o, block_mask: int, sm_scale, mode, blk_q, b
     _check(lib().sattn_fwd_block_sparse(_ref(q), _ref(k), _ref(v), _ref(o), ctypes.c_void_p(block_mask),
                                         float(sm_scale), mode, blk_q, blk_k, ctypes.c_void_p(ws), ws_bytes,
                                         ctypes.c_void_p(stream)), "sattn_fwd_block_sparse")
+
+
+def sattn_error_stats(a, ref, out: int, stream: int):
+    _check(lib().sattn_error_stats(_ref(a), _ref(ref), ctypes.c_void_p(out), ctypes.c_void_p(stream)),
+           "sattn_error_stats")
 
 
 def sattn_debug_qk_int32(qk: sattn_quant, b, h, q0, nq, k0, nk, out: int, stream: int):
@@ -225,6 +231,15 @@ def cross_fwd(q, k, v, mode=SATTN_MODE_BF16, sm_scale=None, out=None, workspace=
     sattn_cross_fwd(tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(o), _resolve(sm_scale, d), mode,
                     ws.data_ptr(), ws.numel(), _stream())
     return o
+
+
+def error_stats(a, ref):
+    """Per-head fp64 sums [sum (a-ref)^2, sum ref^2, sum a*ref, sum a^2] of two [B, H, N, d] bf16 GPU tensors
+    through sattn_error_stats.  Returns a [B, H, 4] float64 GPU tensor."""
+    B, H = a.shape[0], a.shape[1]
+    out = torch.empty((B, H, 4), dtype=torch.float64, device=a.device)
+    sattn_error_stats(tensor_desc(a), tensor_desc(ref), out.data_ptr(), _stream())
+    return out
 
 
 class Quantized:

@@ -24,7 +24,8 @@ import torch
 
 # Distribution recipes (K offset per channel; extras):
 #   "tiny"     : Q, V ~ N(0,1); K ~ N(0,1) + U(-4, 4) per channel; channel 0 of K is all zeros.
-#   "outlier"  : Q, K, V ~ N(0,1); K + N(0, 3^2) per channel; 4 distinct channels of K scaled x10.
+#   "outlier"  : Q, K, V ~ N(0,1); K + N(0, 3^2) per channel; 4 distinct channels of K scaled x10
+#                (x outlier_scale).
 #   "zeroblk"  : Q, K, V ~ N(0,1); K + N(0, 3^2) per channel; 1 % of the 64-token K blocks all zero.
 #   "plain"    : Q, K, V ~ N(0,1).
 DISTS = ("tiny", "outlier", "zeroblk", "plain")
@@ -45,6 +46,7 @@ class Workload:
     dist: str
     seed: int
     modes: Tuple[int, ...]
+    outlier_scale: float = 10.0  # factor of the 4 outlier channels of K ("outlier" recipe)
 
     @property
     def ops(self) -> float:
@@ -104,7 +106,7 @@ def head_inputs(w: Workload, b: int, h: int, seed: int | None = None):
         k += (3.0 * rng.standard_normal((1, d))).astype(np.float32)
         if w.dist == "outlier":
             ch = rng.choice(d, size=4, replace=False)
-            k[:, ch] *= np.float32(10.0)
+            k[:, ch] *= np.float32(w.outlier_scale)
         else:
             nblk = (w.Nkv + 63) // 64
             nzero = int(round(0.01 * nblk))
@@ -174,3 +176,17 @@ def kept_pairs(w: Workload, mask: np.ndarray) -> int:
     rq = np.minimum(MASK_QBLK, w.Nq - np.arange(nqm) * MASK_QBLK)
     rk = np.minimum(MASK_KBLK, w.Nkv - np.arange(nkm) * MASK_KBLK)
     return int(np.einsum("bhij,i,j->", (np.asarray(mask) != 0).astype(np.int64), rq, rk))
+
+
+# ---------------------------------------------------------------- per-layer error probe
+PROBE_SEED = 3000
+
+
+def probe_layers(n_layers: int, base: Workload, seed: int = PROBE_SEED):
+    """Synthetic layers of different quantization sensitivity for the per-layer error probe: every layer follows the
+    "outlier" recipe of ``base``'s shape with its own K outlier factor, drawn from (1, 3, 10, 30, 100) by a seeded
+    PCG64 stream; iteration t of layer l draws its tensors with seed ``seed + 100 * l + t``."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    factors = rng.choice(np.array([1.0, 3.0, 10.0, 30.0, 100.0]), size=n_layers)
+    return [dataclasses.replace(base, name=f"{base.name}-layer{l}", dist="outlier", outlier_scale=float(f),
+                                seed=seed + 100 * l) for l, f in enumerate(factors)]

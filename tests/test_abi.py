@@ -132,6 +132,16 @@ def test_argument_errors_are_caught_on_the_host(S):
     assert sparse(k=k_long) == S.SATTN_ERR_UNSUPPORTED
     assert sparse(ws=P + 16) == S.SATTN_ERR_INVALID_ARG            # reaches the workspace check
     assert sparse(k=_t(S, P, 1, 2, 200, 64), ws=P + 16) == S.SATTN_ERR_INVALID_ARG  # K rows != V rows
+    # error stats: both outputs of one shape, an 8-byte aligned output, d in {64, 128}, at most 65535 heads
+    es = L.sattn_error_stats
+    assert es(None, byref(o), ctypes.c_void_p(P), None) == S.SATTN_ERR_INVALID_ARG
+    assert es(byref(o), byref(o), None, None) == S.SATTN_ERR_INVALID_ARG
+    assert es(byref(o), byref(_t(S, P, 1, 2, 255, 64)), ctypes.c_void_p(P), None) == S.SATTN_ERR_INVALID_ARG
+    assert es(byref(o), byref(o), ctypes.c_void_p(P + 4), None) == S.SATTN_ERR_INVALID_ARG
+    o96 = _t(S, P, 1, 2, 256, 96)
+    assert es(byref(o96), byref(o96), ctypes.c_void_p(P), None) == S.SATTN_ERR_UNSUPPORTED
+    many = _t(S, P, 1, 65536, 1, 64)
+    assert es(byref(many), byref(many), ctypes.c_void_p(P), None) == S.SATTN_ERR_UNSUPPORTED
     # cross-attention and the quantized entry points validate the same way
     assert L.sattn_cross_fwd(byref(q), byref(k), byref(v), byref(o), 0.0, 2, None, 0, None) == S.SATTN_ERR_WORKSPACE
     assert L.sattn_fwd_quantized(None, None, None, byref(o), 0.0, 2, None) == S.SATTN_ERR_INVALID_ARG
