@@ -167,7 +167,11 @@ __device__ __forceinline__ v16f mfma_e4m3(const v8i& a, const v8i& b, const v16f
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 __device__ __forceinline__ int pack_e4m3(float lo0, float lo1, float hi0, float hi1) {
-  const int w = __builtin_amdgcn_cvt_pk_fp8_f32(lo0, lo1, 0, false);
+  // the two conversions write the low and the high half of the word, so its prior content is never read: start
+  // from whatever the register holds instead of a zeroed one
+  int w;
+  asm volatile("" : "=v"(w));
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(lo0, lo1, w, false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(hi0, hi1, w, true);
 }
 
@@ -352,7 +356,9 @@ __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
   auto softmax = [&](const SAcc (&acc)[2], float f, int valid, PTile<MODE>& p, auto tail_tag) {
     constexpr bool TAIL = decltype(tail_tag)::value;
     auto in_seq = [&](int bm, int r) { return !TAIL || (32 * g + 16 * bm + r < valid); };
-    // the score of element (bm, r) as a float: S (bf16 op) or S * 2^-26 (unbiased INT8 result)
+    // the score of element (bm, r) as a float: S (bf16 op) or S * 2^-26 (unbiased INT8 result, exact).  Folding the
+    // bias into the FMA's addend instead would round that addend (about 2^23 units of S) once per tile; the
+    // resulting shift flips E4M3 roundings of P often enough to be visible in O, so the subtraction stays exact.
     auto score = [&](int bm, int r) {
       if constexpr (MODE == 0) return acc[bm][r];
       else return __int_as_float(acc[bm][r]) - bias_f;
@@ -381,7 +387,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
     const float fe = (MODE == 0) ? f : f * 0x1p26f;         // scale of the stored scores
     // mode 2 keeps 448 p (= 2^(x - m + log2 448)) so that the E4M3 conversion needs no multiply
     const float nb = ((MODE == 2) ? 8.807354922057604f : 0.0f) - mnew;
-    float lp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float lp[4];
     if constexpr (MODE == 2) {
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
@@ -391,7 +397,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
         for (int e = 0; e < 4; ++e) {
           pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(score(bm, r0 + e), fe, nb));
           if (!in_seq(bm, r0 + e)) pe[e] = 0.0f;
-          lp[e] += pe[e];
+          lp[e] = (w == 0) ? pe[e] : lp[e] + pe[e];
         }
         p.w[w] = pack_e4m3(pe[0], pe[1], pe[2], pe[3]);
       }
@@ -403,7 +409,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
         for (int e = 0; e < 8; ++e) {
           float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(score(bm, r0 + e), fe, nb));
           if (!in_seq(bm, r0 + e)) pe = 0.0f;
-          lp[e & 3] += pe;
+          lp[e & 3] = (j == 0 && e < 4) ? pe : lp[e & 3] + pe;
           p.b[j][e] = (__bf16)pe;
         }
       }
