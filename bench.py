@@ -319,16 +319,21 @@ def main():
         step()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event between consecutive steps as well, for the per-step spread (median, min, max)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     e0.record(stream)
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for i in range(args.steps):
         step()
+        marks[i + 1].record(stream)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = e0.elapsed_time(e1) / args.steps
     value = w.ops / (ms_per_step * 1e-3) / 1e12
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
 
     # the dominant kernel alone: attention on prepared operands, HIP events on the same stream
     qz = sattn.Quantized(w.B, w.H, w.Nq, w.Nkv, w.d, w.blk_q, mode, dev)
@@ -370,6 +375,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_median_min_max": [round(step_ms[len(step_ms) // 2], 4), round(step_ms[0], 4),
+                                       round(step_ms[-1], 4)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -390,7 +397,7 @@ def main():
             "frac": round(achieved / PEAK_TOPS[mode], 4),
             "traffic": traffic_detail["total_bytes"] if traffic_detail else None,
             "traffic_detail": traffic_detail,
-            "kernel": (f"attn_kernel<0, {w.d}>" if mode == 0 else f"attn_pipe_kernel<{mode}, {w.d}, 4>"),
+            "kernel": f"attn_pipe_kernel<{mode}, {w.d}, 4>",
             "ops_per_launch": w.ops,
         },
         "wall_s_timed_region": round(wall, 3),
