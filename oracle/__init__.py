@@ -17,6 +17,8 @@ Functions mirror the steps of the method:
 * ``qk_int``      exact integer scores
 * ``attn_emulate``  tile-faithful replay of dequant + online softmax + P*V + epilogue (modes 0/1/2)
 * ``attn_ref_fp64`` exact attention in fp64 (what the quantized modes approximate)
+* ``quant_blocks``, ``linear_w8a8``, ``linear_w8a16``  the 128 x 128 per-block quantized linear layer
+  (``linear_oracle.c``)
 
 Parity pins for all of them are in ``tests/test_oracle_*.py``.
 """
@@ -29,7 +31,7 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "sattn_oracle.c")
+_SRCS = [os.path.join(_HERE, "sattn_oracle.c"), os.path.join(_HERE, "linear_oracle.c")]
 _LIB_PATH = os.path.join(_HERE, "libsattn_oracle.so")
 
 MODE_BF16 = 0
@@ -40,10 +42,11 @@ GCC_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp
 
 
 def build(force: bool = True) -> str:
-    """Compile ``sattn_oracle.c`` into ``libsattn_oracle.so`` next to it (plain gcc, no HIP)."""
+    """Compile ``sattn_oracle.c`` and ``linear_oracle.c`` into ``libsattn_oracle.so`` next to them (plain gcc, no
+    HIP)."""
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp"
-        subprocess.check_call(["gcc", *GCC_FLAGS, "-o", tmp, _SRC, "-lm"])
+        subprocess.check_call(["gcc", *GCC_FLAGS, "-o", tmp, *_SRCS, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -78,6 +81,11 @@ def lib() -> ctypes.CDLL:
         L.orc_attn_ref_fp64_masked.argtypes = [i32, i32, f64, P, P, P, P, i32, P, i32, P]
         L.orc_attn_ref_fp64_masked.restype = None
         L.orc_max_threads.argtypes, L.orc_max_threads.restype = [], i32
+        L.orc_quant_blocks.argtypes, L.orc_quant_blocks.restype = [P, i32, i32, i64, i32, i32, P, P], None
+        L.orc_linear_w8a8.argtypes = [P, P, P, P, P, i32, i32, i32, i32, P, P]
+        L.orc_linear_w8a8.restype = None
+        L.orc_linear_w8a16.argtypes = [P, P, P, P, i32, i32, i32, i32, P, P]
+        L.orc_linear_w8a16.restype = None
         _lib = L
     return _lib
 
@@ -263,3 +271,50 @@ def error_stats(a_bits, r_bits) -> np.ndarray:
     assert a.shape == r.shape
     d = a - r
     return np.array([np.sum(d * d), np.sum(r * r), np.sum(a * r), np.sum(a * a)])
+
+
+# ---------------------------------------------------------------- the quantized linear layer (linear_oracle.c)
+LINEAR_BLK = 128
+
+
+def quant_blocks(x_bits, blk: int = LINEAR_BLK):
+    """Per-block INT8 of a bf16 matrix [rows, cols] (16-bit patterns) in blk x blk blocks: (codes int8 [rows, cols],
+    scales float32 [ceil(rows/blk), ceil(cols/blk)])."""
+    x = _dense(np.asarray(x_bits), np.uint16)
+    rows, cols = x.shape
+    codes = np.empty((rows, cols), np.int8)
+    scales = np.empty((_nblk(rows, blk), _nblk(cols, blk)), np.float32)
+    lib().orc_quant_blocks(_ptr(x), rows, cols, cols, blk, blk, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def linear_w8a8(xq, sx, wq, sw, bias_bits=None, blk: int = LINEAR_BLK):
+    """W8A8 linear y = sum_kb s_x s_w S_kb + b in fp64.  xq [M, K] int8 with sx [ceil(M/blk), K/blk]; wq [N, K]
+    with sw [ceil(N/blk), K/blk]; bias: bf16 patterns [N] or None.  Returns (y [M, N], mag [M, N])."""
+    xq, wq = _dense(xq, np.int8), _dense(wq, np.int8)
+    sx, sw = _dense(sx, np.float32), _dense(sw, np.float32)
+    M, K = xq.shape
+    N = wq.shape[0]
+    assert wq.shape[1] == K and K % blk == 0
+    assert sx.shape == (_nblk(M, blk), K // blk) and sw.shape == (_nblk(N, blk), K // blk)
+    b = None if bias_bits is None else _dense(np.asarray(bias_bits), np.uint16)
+    assert b is None or b.shape == (N,)
+    y = np.empty((M, N), np.float64)
+    mag = np.empty((M, N), np.float64)
+    lib().orc_linear_w8a8(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), _ptr(b), M, N, K, blk, _ptr(y), _ptr(mag))
+    return y, mag
+
+
+def linear_w8a16(x_bits, wq, sw, bias_bits=None, blk: int = LINEAR_BLK):
+    """W8A16 linear y = sum_kb s_w (x . Wq)_kb + b in fp64.  x: bf16 patterns [M, K]; wq, sw, bias as for
+    linear_w8a8.  Returns (y [M, N], mag [M, N])."""
+    x, wq, sw = _dense(np.asarray(x_bits), np.uint16), _dense(wq, np.int8), _dense(sw, np.float32)
+    M, K = x.shape
+    N = wq.shape[0]
+    assert wq.shape[1] == K and K % blk == 0 and sw.shape == (_nblk(N, blk), K // blk)
+    b = None if bias_bits is None else _dense(np.asarray(bias_bits), np.uint16)
+    assert b is None or b.shape == (N,)
+    y = np.empty((M, N), np.float64)
+    mag = np.empty((M, N), np.float64)
+    lib().orc_linear_w8a16(_ptr(x), _ptr(wq), _ptr(sw), _ptr(b), M, N, K, blk, _ptr(y), _ptr(mag))
+    return y, mag

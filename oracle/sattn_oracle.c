@@ -120,7 +120,7 @@ void orc_k_mean(const uint16_t* k, int n, int d, long long ld, float* mu) {
 /* otherwise inv = 127/a, scale = a/127, code = clamp(rint(x*inv), -127, 127), rint ties to even.    */
 /* x: fp32 [rows, d] dense.  codes: [rows, d].                                                        */
 /* ------------------------------------------------------------------------------------------------ */
-static void quant_i8_block(const float* x, int rows, int d, int8_t* codes, float* scale) {
+void orc_quant_i8_rows(const float* x, int rows, int d, int8_t* codes, float* scale) {
   float a = 0.0f;
   for (long long i = 0; i < (long long)rows * d; ++i) {
     float v = fabsf(x[i]);
@@ -151,7 +151,7 @@ void orc_quant_q(const uint16_t* q, int n, int d, long long ld, int blk, int8_t*
     int r0 = b * blk, rows = (n - r0) < blk ? (n - r0) : blk;
     for (int r = 0; r < rows; ++r)
       for (int c = 0; c < d; ++c) x[(long long)r * d + c] = orc_bf16_to_f32(q[(long long)(r0 + r) * ld + c]);
-    quant_i8_block(x, rows, d, codes + (long long)r0 * d, &scales[b]);
+    orc_quant_i8_rows(x, rows, d, codes + (long long)r0 * d, &scales[b]);
   }
   free(x);
 }
@@ -167,7 +167,7 @@ void orc_quant_k(const uint16_t* k, int n, int d, long long ld, const float* mu,
     for (int r = 0; r < rows; ++r)
       for (int c = 0; c < d; ++c)
         x[(long long)r * d + c] = orc_bf16_to_f32(k[(long long)(r0 + r) * ld + c]) - mu[c];
-    quant_i8_block(x, rows, d, codes + (long long)r0 * d, &scales[b]);
+    orc_quant_i8_rows(x, rows, d, codes + (long long)r0 * d, &scales[b]);
   }
   free(x);
 }
