@@ -211,6 +211,63 @@ def layer_probe(args):
     }), flush=True)
 
 
+def linear_layers(args):
+    """The quantized linear layer at the Wan-14B 720p shapes (75 600 tokens): one JSON line per shape with W8A8 (the
+    headline: effective TOPS over 2 M N K), W8A16, the GEMM kernel alone on prepared codes, the activation
+    quantization alone, and torch's bf16 linear (hipBLASLt) on the same tensors as context."""
+    import torch
+
+    from quantized_attention_05_amd import sattn
+    from quantized_attention_05_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    for name in ("wan14b-720p-ffn-up", "wan14b-720p-ffn-down", "wan14b-720p-proj"):
+        w = wl.LINEAR_WORKLOADS[name]
+        x, wt, b = wl.linear_device_inputs(w, dev)
+        wq, sw = sattn.quantize_blocks(wt)
+        y = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(max(sattn.sattn_linear_workspace_bytes(w.M, w.N, w.K, m) for m in (0, 1)), dtype=torch.uint8,
+                         device=dev)
+        xq, sx = sattn.quantize_blocks(x)
+        ms8 = timed(lambda: sattn.linear(x, wq, sw, b, mode=sattn.SATTN_LINEAR_W8A8, out=y, workspace=ws), args.steps)
+        ms16 = timed(lambda: sattn.linear(x, wq, sw, b, mode=sattn.SATTN_LINEAR_W8A16, out=y, workspace=ws),
+                     args.steps)
+        gemm8 = timed(lambda: sattn.linear_quantized(xq, sx, wq, sw, b, out=y), args.steps)
+        quant = timed(lambda: sattn.quantize_blocks(x), args.steps)
+        bf16 = timed(lambda: torch.nn.functional.linear(x, wt, b), args.steps)
+        tops = lambda ms: round(w.ops / (ms * 1e-3) / 1e12, 1)
+        print(json.dumps({
+            "metric": f"quantized linear layer TOPS (2 M N K), Wan-14B 720p {name.split('720p-')[1]}",
+            "value": tops(ms8), "unit": "TOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms8, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "int8 (W8A8, 128x128 blocks)", "data": "synthetic: N(0,1) x with x20 outlier channels, "
+            "N(0,1/K) weights, drawn on the GPU (recipe in DESIGN.md)",
+            "config": {"workload": f"{name} linear", "M": w.M, "N": w.N, "K": w.K},
+            "pct_int8_mfma_peak": round(100 * w.ops / (ms8 * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2),
+            "w8a8_ms": round(ms8, 4), "w8a16_ms": round(ms16, 4), "w8a16_tops": tops(ms16),
+            "gemm_w8a8_kernel_ms": round(gemm8, 4), "gemm_w8a8_kernel_tops": tops(gemm8),
+            "quantize_x_ms": round(quant, 4),
+            "quantize_x_gbps": round(w.M * w.K * 3 / (quant * 1e-3) / 1e9, 1),
+            "torch_bf16_linear_ms": round(bf16, 4), "torch_bf16_linear_tops": tops(bf16),
+        }), flush=True)
+        del x, wt, b, wq, sw, y, ws, xq, sx
+        torch.cuda.empty_cache()
+
+
 def cpu_baseline(w, mode: int, budget_s: float):
     """The oracle, as it stands, on a bounded sample: quantize one head in full, then emulate query blocks of
     that head until about `budget_s` seconds of CPU time are spent.  Extrapolated linearly to the whole call
@@ -260,7 +317,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan14b-720p",
-                    help="a name from quantized_attention_05_amd.workloads.WORKLOADS, 'layersel', 'sparse' or 'probe'")
+                    help="a name from quantized_attention_05_amd.workloads.WORKLOADS, 'layersel', 'sparse', 'probe' or "
+                         "'linear'")
     ap.add_argument("--mode", type=int, default=2, choices=[0, 1, 2])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -292,6 +350,9 @@ def main():
         return
     if args.workload == "probe":
         layer_probe(args)
+        return
+    if args.workload == "linear":
+        linear_layers(args)
         return
 
     import torch

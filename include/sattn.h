@@ -176,6 +176,54 @@ sattn_status sattn_fwd_block_sparse(const sattn_tensor* q, const sattn_tensor* k
  * NULL or mismatched tensors, SATTN_ERR_UNSUPPORTED for d outside {64, 128} or B*H > 65535. */
 sattn_status sattn_error_stats(const sattn_tensor* a, const sattn_tensor* ref, double* out, sattn_stream_t stream);
 
+/* ---------------------------------------------------------------------------------------------------------------
+ * Quantized linear layer (TMAP I2V write-up, section "FFN性能优化", subsection "线性层量化"): the weights of the
+ * linear layers are stored in INT8 with one scale per 128 x 128 block.  W8A8 also quantizes the activations per
+ * 128 x 128 block and multiplies in 8 bits; W8A16, the fallback for layers whose quality suffers, keeps bf16
+ * activations against the same 8-bit weights.  The layer is y = x W^T + b with x [M, K], W [N, K] (output x input
+ * features) and b [N]: the addmm of the model's FLOP profile (section "Attention 性能优化 / 背景").
+ * --------------------------------------------------------------------------------------------------------------- */
+#define SATTN_LINEAR_BLK 128
+
+typedef enum { SATTN_LINEAR_W8A8 = 0, SATTN_LINEAR_W8A16 = 1 } sattn_linear_mode;
+
+/* Per-block INT8 of a bf16 matrix x [rows, cols] (row stride ld elements).  For every 128 x 128 block (the last row
+ * block may be shorter): a = max |v|; a < 2^-100 gives scale 0 and codes 0, else scale = a/127 and
+ * code = clamp(rint(v * (127/a)), -127, 127) in fp32 with ties to even.  codes: int8 [rows, cols] dense; scales:
+ * float [ceil(rows/128), cols/128] row-major.  Device memory; x and codes 16-byte aligned, scales 4-byte aligned.
+ * Prepares a weight once, ahead of the calls that use it.  Errors: SATTN_ERR_INVALID_ARG for a NULL or misaligned
+ * pointer, rows < 1, ld < cols or ld not a multiple of 8; SATTN_ERR_UNSUPPORTED for cols not a positive multiple of
+ * 128, or rows or cols above 2^28. */
+sattn_status sattn_quantize_blocks(const void* x, int rows, int cols, int64_t ld, int8_t* codes, float* scales,
+                                   sattn_stream_t stream);
+
+/* Workspace of sattn_linear in bytes: W8A8 the activation codes and their scales (M*K, then
+ * 4*ceil(M/128)*(K/128), each part 256-byte aligned), W8A16 the weight codes widened to bf16 (2*N*K).  0 for an
+ * invalid shape or mode. */
+size_t sattn_linear_workspace_bytes(int M, int N, int K, int mode);
+
+/* W8A8 linear on prepared operands: y[m, n] = sum over the 128-wide K blocks kb of
+ * (sx[m/128, kb] * sw[n/128, kb]) * (the exact int32 dot product of the codes over kb) + bias[n], accumulated in
+ * fp32 in K-block order and rounded to bf16.  xq: int8 [M, K] dense with sx [ceil(M/128), K/128]; wq: int8 [N, K]
+ * dense with sw [ceil(N/128), K/128] (both as written by sattn_quantize_blocks); bias: bf16 [N] or NULL; y: bf16
+ * [M, N], row stride ldy (>= N), 2-byte aligned (rows that start 16-byte aligned are written 16 bytes at a time).  K: a positive multiple of 128, at most 2^20.
+ * Device memory throughout; allocates nothing.  Errors: SATTN_ERR_INVALID_ARG for NULL or misaligned pointers or a
+ * bad stride; SATTN_ERR_UNSUPPORTED for a K outside the above, M or N above 2^28, or more than 2^31 - 1 output
+ * tiles of 128 x 128. */
+sattn_status sattn_linear_quantized(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
+                                    const void* bias, void* y, int64_t ldy, int M, int N, int K, sattn_stream_t stream);
+
+/* The quantized linear layer y = x W^T + bias for bf16 activations x [M, K] (row stride ldx, a multiple of 8;
+ * 16-byte aligned) and a weight prepared by sattn_quantize_blocks (wq [N, K], sw).
+ *   SATTN_LINEAR_W8A8 : x is quantized per 128 x 128 block into the workspace, then as sattn_linear_quantized.
+ *   SATTN_LINEAR_W8A16: y[m, n] = sum over kb of sw[n/128, kb] * (x . wq over kb, fp32) + bias[n]; the weight codes
+ *                       are widened to bf16 in the workspace (exact), x is used as given.
+ * ws: device, 256-byte aligned, at least sattn_linear_workspace_bytes(M, N, K, mode) bytes.  Errors: as
+ * sattn_linear_quantized (ldx above 2^23 is SATTN_ERR_UNSUPPORTED), plus SATTN_ERR_INVALID_ARG for an unknown mode
+ * and SATTN_ERR_WORKSPACE for a missing or small workspace. */
+sattn_status sattn_linear(const void* x, int64_t ldx, const int8_t* wq, const float* sw, const void* bias, void* y,
+                          int64_t ldy, int M, int N, int K, int mode, void* ws, size_t ws_bytes, sattn_stream_t stream);
+
 /* Test hook: the int32 scores S = q_codes . k_codes^T of one (b, h) for query rows [q0, q0+nq) and keys
  * [k0, k0+nk), computed with the same INT8 matrix-core path as the attention kernel.
  * out: device int32 [nq, nk] row-major.  Rows/keys must lie inside the padded code arrays. */

@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstring>
 
+#include "linear_internal.h"
 #include "sattn_internal.h"
 
 using namespace sattn;
@@ -322,6 +323,85 @@ sattn_status sattn_debug_qk_int32(const sattn_quant* qk, int b, int h, int q0, i
   const int nq_pad = cdiv(qk->Nq, qk->blk_q) * qk->blk_q, nk_pad = cdiv(qk->Nkv, kTile) * kTile;
   if ((int64_t)q0 + nq > nq_pad || (int64_t)k0 + nk > nk_pad) return SATTN_ERR_INVALID_ARG;
   return hip_status(launch_debug_qk(quant_arg(*qk), b, h, q0, nq, k0, nk, out, reinterpret_cast<hipStream_t>(stream)));
+}
+
+// ---- quantized linear layer
+sattn_status sattn_quantize_blocks(const void* x, int rows, int cols, int64_t ld, int8_t* codes, float* scales,
+                                   sattn_stream_t stream) {
+  if (!x || !codes || !scales || rows < 1 || cols < 1) return SATTN_ERR_INVALID_ARG;
+  if (cols % kLinBlk != 0 || rows > (1 << 28) || cols > (1 << 28)) return SATTN_ERR_UNSUPPORTED;
+  if (ld < cols || ld % 8 != 0 || !aligned16(x) || !aligned16(codes) || reinterpret_cast<uintptr_t>(scales) % 4)
+    return SATTN_ERR_INVALID_ARG;
+  return hip_status(launch_quant_blocks(static_cast<const uint16_t*>(x), rows, cols, ld, codes, scales,
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t sattn_linear_workspace_bytes(int M, int N, int K, int mode) {
+  if (M < 1 || N < 1 || K < kLinBlk || K % kLinBlk != 0) return 0;
+  if (mode == SATTN_LINEAR_W8A8) return align_up((size_t)M * K) + align_up((size_t)cdiv(M, kLinBlk) * (K / kLinBlk) * 4);
+  if (mode == SATTN_LINEAR_W8A16) return align_up((size_t)N * K * 2);
+  return 0;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shape and output checks shared by the linear entry points.
+sattn_status check_linear(const void* y, int64_t ldy, int M, int N, int K, const void* bias) {
+  if (!y || M < 1 || N < 1 || K < 1) return SATTN_ERR_INVALID_ARG;
+  if (K % kLinBlk != 0 || K > (1 << 20) || M > (1 << 28) || N > (1 << 28)) return SATTN_ERR_UNSUPPORTED;
+  if ((int64_t)cdiv(M, kLinBlk) * cdiv(N, kLinBlk) > INT32_MAX) return SATTN_ERR_UNSUPPORTED;
+  if (ldy < N || reinterpret_cast<uintptr_t>(y) % 2) return SATTN_ERR_INVALID_ARG;
+  if (bias && reinterpret_cast<uintptr_t>(bias) % 2) return SATTN_ERR_INVALID_ARG;
+  return SATTN_OK;
+}
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+sattn_status sattn_linear_quantized(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
+                                    const void* bias, void* y, int64_t ldy, int M, int N, int K, sattn_stream_t stream) {
+  if (!xq || !sx || !wq || !sw) return SATTN_ERR_INVALID_ARG;
+  sattn_status st = check_linear(y, ldy, M, N, K, bias);
+  if (st != SATTN_OK) return st;
+  if (!aligned16(xq) || !aligned16(wq) || !aligned4(sx) || !aligned4(sw)) return SATTN_ERR_INVALID_ARG;
+  LinearArg p{reinterpret_cast<const uint8_t*>(xq), K, reinterpret_cast<const uint8_t*>(wq), K, sx, sw,
+              static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), ldy, M, N, K};
+  return hip_status(launch_linear(true, p, reinterpret_cast<hipStream_t>(stream)));
+}
+
+sattn_status sattn_linear(const void* x, int64_t ldx, const int8_t* wq, const float* sw, const void* bias, void* y,
+                          int64_t ldy, int M, int N, int K, int mode, void* ws, size_t ws_bytes, sattn_stream_t stream) {
+  if (!x || !wq || !sw) return SATTN_ERR_INVALID_ARG;
+  if (mode != SATTN_LINEAR_W8A8 && mode != SATTN_LINEAR_W8A16) return SATTN_ERR_INVALID_ARG;
+  sattn_status st = check_linear(y, ldy, M, N, K, bias);
+  if (st != SATTN_OK) return st;
+  if (ldx < K || ldx % 8 != 0 || !aligned16(x) || !aligned16(wq) || !aligned4(sw)) return SATTN_ERR_INVALID_ARG;
+  if (ldx >= (int64_t{1} << 23)) return SATTN_ERR_UNSUPPORTED;  // a 128-row tile of x must span below 2^31 bytes
+  const size_t need = sattn_linear_workspace_bytes(M, N, K, mode);
+  if (!ws || ws_bytes < need) return SATTN_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return SATTN_ERR_INVALID_ARG;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  hipError_t e;
+  if (mode == SATTN_LINEAR_W8A8) {
+    int8_t* xq = reinterpret_cast<int8_t*>(base);
+    float* sx = reinterpret_cast<float*>(base + align_up((size_t)M * K));
+    if ((e = launch_quant_blocks(static_cast<const uint16_t*>(x), M, K, ldx, xq, sx, s)) != hipSuccess)
+      return hip_status(e);
+    LinearArg p{reinterpret_cast<const uint8_t*>(xq), K, reinterpret_cast<const uint8_t*>(wq), K, sx, sw,
+                static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), ldy, M, N, K};
+    return hip_status(launch_linear(true, p, s));
+  }
+  uint16_t* wb = reinterpret_cast<uint16_t*>(base);
+  if ((e = launch_codes_to_bf16(wq, wb, (int64_t)N * K, s)) != hipSuccess) return hip_status(e);
+  LinearArg p{static_cast<const uint8_t*>(x), ldx * 2, reinterpret_cast<const uint8_t*>(wb), (int64_t)K * 2, nullptr,
+              sw, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), ldy, M, N, K};
+  return hip_status(launch_linear(false, p, s));
 }
 
 }  // extern "C"

@@ -1,0 +1,360 @@
+// Quantized linear layer y = x W^T + b with 128 x 128 per-block INT8 (TMAP I2V write-up, section "FFN性能优化",
+// subsection "线性层量化": 8-bit linear weights in 128 x 128 blocks; W8A8 computes in 8 bits, W8A16 keeps the 8-bit
+// weights and 16-bit activations for the layers that need it).
+//
+// Kernels:
+//   quant_blocks_kernel   one workgroup per 128 x 128 block of a bf16 matrix: block max, INT8 codes, block scale
+//                         (the symmetric rule of the attention blocks: scale a/127, codes rint(v * 127/a)).
+//   codes_to_bf16_kernel  INT8 codes to bf16 (exact: |code| <= 127 needs 7 bits), the W8A16 weight operand.
+//   linear_kernel<A8>     the GEMM.  A workgroup owns one 128 x 128 output tile, which is exactly one (row block,
+//                         column block) pair of scale blocks, so every 128-wide K block has one scale factor per
+//                         workgroup: s_x s_w (W8A8) or s_w (W8A16).  Four waves each own 64 x 64 of the tile as
+//                         2 x 2 blocks of 32 x 32 on the matrix cores (v_mfma_i32_32x32x32_i8, or
+//                         v_mfma_f32_32x32x16_bf16).  The matrix cores accumulate one K block exactly (int32) or in
+//                         fp32; at its end the partial sums are scaled and added to the fp32 accumulators.
+//                         Operands stream through a 4-stage LDS ring of 64-byte row slices with direct-to-LDS
+//                         buffer loads three stages ahead.
+#include <algorithm>
+#include <type_traits>
+
+#include "linear_internal.h"
+#include "sattn_internal.h"
+
+namespace sattn {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+constexpr int kLinThreads = 256;
+
+__device__ __forceinline__ float bf16_value(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ uint32_t code_i8(float x, float inv) {
+  float q = rintf(x * inv);
+  q = fminf(fmaxf(q, -127.0f), 127.0f);
+  return (uint32_t)(uint8_t)(int8_t)q;
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// Per-block INT8.  Thread t covers columns [8 (t % 16), +8) of rows t / 16 + 16 i, i = 0..7, of its block.
+__global__ void __launch_bounds__(kLinThreads) quant_blocks_kernel(const uint16_t* __restrict__ x, int rows,
+                                                                   int64_t ld, int8_t* __restrict__ codes, int cols,
+                                                                   float* __restrict__ scales) {
+  const int bj = blockIdx.x, bi = blockIdx.y;
+  const int r0 = bi * kLinBlk, c0 = bj * kLinBlk;
+  const int nr = min(kLinBlk, rows - r0);
+  const int cg = threadIdx.x & 15, rr = threadIdx.x >> 4;
+  uint4 raw[8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = rr + 16 * i;
+    raw[i] = (r < nr) ? *reinterpret_cast<const uint4*>(x + (int64_t)(r0 + r) * ld + c0 + 8 * cg)
+                      : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(bf16_value((w[e / 2] >> (16 * (e & 1))) & 0xFFFFu)));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  __shared__ float wmax[kLinThreads / 64];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  const float a = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const bool zero = !(a >= kGuard);
+  const float inv = zero ? 0.0f : 127.0f / a;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = rr + 16 * i;
+    if (r >= nr) continue;
+    const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      lo |= code_i8(bf16_value((w[e / 2] >> (16 * (e & 1))) & 0xFFFFu), inv) << (8 * e);
+      hi |= code_i8(bf16_value((w[2 + e / 2] >> (16 * (e & 1))) & 0xFFFFu), inv) << (8 * e);
+    }
+    *reinterpret_cast<uint2*>(codes + (int64_t)(r0 + r) * cols + c0 + 8 * cg) = make_uint2(lo, hi);
+  }
+  if (threadIdx.x == 0) scales[(int64_t)bi * (cols / kLinBlk) + bj] = zero ? 0.0f : a / 127.0f;
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// INT8 codes -> bf16, 16 codes per thread and step.
+__global__ void __launch_bounds__(kLinThreads) codes_to_bf16_kernel(const int8_t* __restrict__ c,
+                                                                    uint16_t* __restrict__ out, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * kLinThreads + threadIdx.x; i < n16; i += (int64_t)gridDim.x * kLinThreads) {
+    const uint4 v = reinterpret_cast<const uint4*>(c)[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int sh = 16 * (q & 1);
+      const float lo = (float)(int8_t)(w[q >> 1] >> sh), hi = (float)(int8_t)(w[q >> 1] >> (sh + 8));
+      o[q] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(out) + 2 * i;
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// The GEMM.
+template <bool A8>
+struct LinGeo {
+  static constexpr int EB = A8 ? 1 : 2;           // bytes per operand element
+  static constexpr int ROW = 64;                  // bytes of one operand row per stage (4 granules of 16 B)
+  static constexpr int SPB = kLinBlk * EB / ROW;  // stages per 128-wide K block: 2 (INT8) or 4 (bf16)
+  static constexpr int KSTEPS = ROW / 32;         // matrix-core k-steps per stage, 32 bytes of K each
+  static constexpr int TILE = kLinBlk * ROW;      // one operand slice: 128 rows x 64 B = 8 KiB
+  static constexpr int STAGE = 2 * TILE;          // activations + weights
+  static constexpr int R = 4;                     // ring stages
+  static constexpr int DIST = R - 1;              // a stage is loaded this many iterations before its use
+  static constexpr int LPT = TILE / (16 * kLinThreads);  // 16-byte loads per thread per slice
+  static constexpr int OPS = 2 * LPT;                    // loads per thread per stage
+  static constexpr int BYTES = R * STAGE;                // 64 KiB; the per-K-block scale list follows
+  static_assert(LPT * 16 * kLinThreads == TILE, "slices split into whole loads");
+};
+
+// XOR swizzle of the 4 granules of a 64-byte LDS row.  The 16 lanes of a quarter-wave read 16 consecutive rows at one
+// logical granule (and the 8 lanes of an eighth, 8 rows); this map sends them to distinct bank groups for 64 and for
+// 32 LDS banks.
+__device__ __forceinline__ int lswz(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+
+// Workgroups are handed to the 8 XCDs round-robin; renumber them so that each XCD gets one contiguous range.
+__device__ __forceinline__ int xcd_order(int wg, int nwg) {
+  const int q = nwg / 8, r = nwg % 8;
+  const int xcd = wg % 8, slot = wg / 8;
+  return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void ring_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
+__device__ __forceinline__ v16i mma_i8(const v4i& a, const v4i& b, const v16i& c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v16f mma_bf16(const v8bf& a, const v8bf& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <bool A8>
+__global__ void __launch_bounds__(kLinThreads, 2) linear_kernel(LinearArg p) {
+  // (the body is device code only: the host pass needs just the signature for the launch stub, and it would drop the
+  // stub over the target builtins and register constraints below)
+#if defined(__HIP_DEVICE_COMPILE__)
+  using G = LinGeo<A8>;
+  using Part = std::conditional_t<A8, v16i, v16f>;  // one K block's partial sums
+  using Opnd = std::conditional_t<A8, v4i, v8bf>;
+  constexpr int R = G::R, DIST = G::DIST;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n32 = lane & 31, g = lane >> 5;
+  const int mtiles = (p.M + kLinBlk - 1) / kLinBlk, ntiles = (p.N + kLinBlk - 1) / kLinBlk;
+  const int nkb = p.K / kLinBlk;
+
+  // output tile: XCD-contiguous ranges, then groups of 8 row tiles walked column tile by column tile, so the
+  // workgroups that run together share both their activation and their weight slices in L2
+  constexpr int GM = 8;
+  const int logical = xcd_order(blockIdx.x, gridDim.x);
+  const int grp = logical / (GM * ntiles);
+  const int first = grp * GM;
+  const int gm = min(GM, mtiles - first);
+  const int within = logical - grp * GM * ntiles;
+  const int mt = first + within % gm, nt = within / gm;
+  const int m0 = mt * kLinBlk, n0 = nt * kLinBlk;
+
+  // the scale factor of every K block of this tile, after the ring
+  float* cs = reinterpret_cast<float*>(smem + G::BYTES);
+  for (int kb = threadIdx.x; kb < nkb; kb += kLinThreads)
+    cs[kb] = A8 ? p.sx[(int64_t)mt * nkb + kb] * p.sw[(int64_t)nt * nkb + kb] : p.sw[(int64_t)nt * nkb + kb];
+  __syncthreads();  // a full workgroup barrier: the list is written with ordinary LDS stores (no tile load in flight yet)
+
+  // buffers over the tile's rows: rows past M (N) lie past the buffer end and read as zero
+  const int arows = min(kLinBlk, p.M - m0), brows = min(kLinBlk, p.N - n0);
+  const auto ra = rows_rsrc(p.a + (int64_t)m0 * p.lda, arows * (int)p.lda);
+  const auto rb = rows_rsrc(p.b + (int64_t)n0 * p.ldb, brows * (int)p.ldb);
+  // load plan: load j of this wave fills LDS granules [(4 j + wave) * 64, +64) of a slice; LDS granule q holds row
+  // q / 4, logical granule (q % 4) ^ lswz(row)
+  int la[G::LPT], lb[G::LPT];
+#pragma unroll
+  for (int j = 0; j < G::LPT; ++j) {
+    const int q = (4 * j + wave) * 64 + lane;
+    const int row = q >> 2, lg = (q & 3) ^ lswz(row);
+    la[j] = row * (int)p.lda + 16 * lg;
+    lb[j] = row * (int)p.ldb + 16 * lg;
+  }
+  auto issue = [&](int t) {
+    uint8_t* st = smem + (t % R) * G::STAGE;
+    const int kbyte = t * G::ROW;
+#pragma unroll
+    for (int j = 0; j < G::LPT; ++j) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(st + (4 * j + wave) * 1024), 16, la[j] + kbyte, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(st + G::TILE + (4 * j + wave) * 1024), 16,
+                                               lb[j] + kbyte, 0, 0, 0);
+    }
+  };
+  // operand reads: 32-row block i of this wave, k-step s: row (64 w + 32 i + lane % 32), logical granule 2 s + lane / 32
+  int ard[2][G::KSTEPS], brd[2][G::KSTEPS];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int arow = 64 * wm + 32 * i + n32, brow = 64 * wn + 32 * i + n32;
+#pragma unroll
+    for (int s = 0; s < G::KSTEPS; ++s) {
+      ard[i][s] = arow * G::ROW + 16 * ((2 * s + g) ^ lswz(arow));
+      brd[i][s] = G::TILE + brow * G::ROW + 16 * ((2 * s + g) ^ lswz(brow));
+    }
+  }
+
+  v16f acc[2][2];
+  Part part[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int T = p.K * G::EB / G::ROW;  // stages (at least SPB >= 2)
+#pragma unroll
+  for (int t = 0; t < DIST; ++t)
+    if (t < T) issue(t);
+
+  // one stage: wait for it, release the slot of stage t + DIST, and run its k-steps on the matrix cores; FRESH (the
+  // first stage of a K block) starts the partial sums from zero
+  auto stage = [&](int t, auto fresh_tag) __attribute__((always_inline)) {
+    constexpr bool FRESH = decltype(fresh_tag)::value;
+    // stage t has landed for every wave once each has waited for its own loads of it
+    if (t + DIST - 1 < T) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DIST - 1) * G::OPS) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    ring_sync();
+    // the slot of stage t + DIST was last read in iteration t - 1, which every wave has finished
+    if (t + DIST < T) issue(t + DIST);
+    const uint8_t* st = smem + (t % R) * G::STAGE;
+#pragma unroll
+    for (int s = 0; s < G::KSTEPS; ++s) {
+      Opnd av[2], bv[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        av[i] = *reinterpret_cast<const Opnd*>(st + ard[i][s]);
+        bv[i] = *reinterpret_cast<const Opnd*>(st + brd[i][s]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          Part c0 = part[i][j];
+          if (FRESH && s == 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) c0[r] = 0;
+          }
+          if constexpr (A8) part[i][j] = mma_i8(av[i], bv[j], c0);
+          else part[i][j] = mma_bf16(av[i], bv[j], c0);
+        }
+    }
+  };
+  for (int kb = 0; kb < nkb; ++kb) {
+    stage(kb * G::SPB, std::true_type{});
+#pragma unroll
+    for (int u = 1; u < G::SPB; ++u) stage(kb * G::SPB + u, std::false_type{});
+    const float c = cs[kb];  // end of the K block: acc += c * partial
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(c, (float)part[i][j][r], acc[i][j][r]);
+  }
+
+  // epilogue through LDS (the ring is free once every wave is past its last stage): the wave writes its 64 x 64
+  // block as bf16 rows of 128 bytes, then stores them 16 bytes per lane.  Lane holds column 32 j + lane % 32 of the
+  // block; register r of block i is row 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  uint16_t* ot = reinterpret_cast<uint16_t*>(smem) + wave * 64 * 64;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int cl = 32 * j + n32;
+    const int n = n0 + 64 * wn + cl;
+    const float bias = (p.bias && n < p.N) ? bf16_value(p.bias[n]) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rl = 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
+        const __bf16 h = (__bf16)(acc[i][j][r] + bias);
+        ot[rl * 64 + cl] = __builtin_bit_cast(uint16_t, h);
+      }
+  }
+  __syncthreads();
+  // 64 rows x 8 granules of 16 bytes per wave block: lane reads granule lane % 8 of rows lane / 8 + 8 q
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int rl = lane / 8 + 8 * q, gc = lane % 8;
+    const int m = m0 + 64 * wm + rl, n = n0 + 64 * wn + 8 * gc;
+    if (m >= p.M || n >= p.N) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(ot + rl * 64 + 8 * gc);
+    uint16_t* dst = p.y + (int64_t)m * p.ldy + n;
+    if (n + 8 <= p.N && (reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
+      *reinterpret_cast<uint4*>(dst) = v;
+    } else {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      const int cnt = min(8, p.N - n);
+      for (int e = 0; e < cnt; ++e) dst[e] = (uint16_t)(w[e / 2] >> (16 * (e & 1)));
+    }
+  }
+#endif
+}
+
+template <bool A8>
+hipError_t launch_linear_t(const LinearArg& p, hipStream_t s) {
+  using G = LinGeo<A8>;
+  const int mtiles = (p.M + kLinBlk - 1) / kLinBlk, ntiles = (p.N + kLinBlk - 1) / kLinBlk;
+  const size_t bytes = G::BYTES + (size_t)(p.K / kLinBlk) * sizeof(float);
+  static bool configured[2] = {false, false};
+  if (!configured[A8]) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_kernel<A8>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+    if (e != hipSuccess) return e;
+    configured[A8] = true;
+  }
+  linear_kernel<A8><<<(unsigned)(mtiles * ntiles), kLinThreads, bytes, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_blocks(const uint16_t* x, int rows, int cols, int64_t ld, int8_t* codes, float* scales,
+                               hipStream_t s) {
+  const dim3 grid((unsigned)(cols / kLinBlk), (unsigned)((rows + kLinBlk - 1) / kLinBlk));
+  quant_blocks_kernel<<<grid, kLinThreads, 0, s>>>(x, rows, ld, codes, cols, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_codes_to_bf16(const int8_t* codes, uint16_t* out, int64_t n, hipStream_t s) {
+  const int64_t n16 = n / 16;
+  const int64_t blocks = std::min<int64_t>((n16 + kLinThreads - 1) / kLinThreads, 8192);
+  codes_to_bf16_kernel<<<(unsigned)std::max<int64_t>(blocks, 1), kLinThreads, 0, s>>>(codes, out, n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_linear(bool w8a8, const LinearArg& p, hipStream_t s) {
+  return w8a8 ? launch_linear_t<true>(p, s) : launch_linear_t<false>(p, s);
+}
+
+}  // namespace sattn

@@ -24,6 +24,10 @@ SATTN_MODE_BF16 = 0
 SATTN_MODE_I8_BF16 = 1
 SATTN_MODE_I8_FP8 = 2
 
+SATTN_LINEAR_BLK = 128
+SATTN_LINEAR_W8A8 = 0
+SATTN_LINEAR_W8A16 = 1
+
 
 class SattnError(RuntimeError):
     def __init__(self, status: int, where: str):
@@ -67,6 +71,10 @@ SYMBOLS = [
     ("sattn_fwd_block_sparse", _I, [_TP, _TP, _TP, _TP, _P, ctypes.c_float, _I, _I, _I, _P, _SZ, _P]),
     ("sattn_error_stats", _I, [_TP, _TP, _P, _P]),
     ("sattn_debug_qk_int32", _I, [_QP, _I, _I, _I, _I, _I, _I, _P, _P]),
+    ("sattn_quantize_blocks", _I, [_P, _I, _I, ctypes.c_int64, _P, _P, _P]),
+    ("sattn_linear_workspace_bytes", _SZ, [_I, _I, _I, _I]),
+    ("sattn_linear_quantized", _I, [_P, _P, _P, _P, _P, _P, ctypes.c_int64, _I, _I, _I, _P]),
+    ("sattn_linear", _I, [_P, ctypes.c_int64, _P, _P, _P, _P, ctypes.c_int64, _I, _I, _I, _I, _P, _SZ, _P]),
 ]
 
 
@@ -302,3 +310,96 @@ def debug_qk_int32(qz: Quantized, b, h, q0, nq, k0, nk):
     out = torch.empty((nq, nk), dtype=torch.int32, device=qz.buf.device)
     sattn_debug_qk_int32(qz.desc, b, h, q0, nq, k0, nk, out.data_ptr(), _stream())
     return out
+
+
+# ---------------------------------------------------------------- quantized linear layer
+def sattn_quantize_blocks(x: int, rows, cols, ld, codes: int, scales: int, stream: int):
+    _check(lib().sattn_quantize_blocks(_P(x), rows, cols, ld, _P(codes), _P(scales), _P(stream)),
+           "sattn_quantize_blocks")
+
+
+def sattn_linear_workspace_bytes(M, N, K, mode) -> int:
+    return int(lib().sattn_linear_workspace_bytes(M, N, K, mode))
+
+
+def sattn_linear_quantized(xq: int, sx: int, wq: int, sw: int, bias: int | None, y: int, ldy, M, N, K, stream: int):
+    _check(lib().sattn_linear_quantized(_P(xq), _P(sx), _P(wq), _P(sw), _P(bias), _P(y), ldy, M, N, K, _P(stream)),
+           "sattn_linear_quantized")
+
+
+def sattn_linear(x: int, ldx, wq: int, sw: int, bias: int | None, y: int, ldy, M, N, K, mode, ws: int, ws_bytes: int,
+                 stream: int):
+    _check(lib().sattn_linear(_P(x), ldx, _P(wq), _P(sw), _P(bias), _P(y), ldy, M, N, K, mode, _P(ws), ws_bytes,
+                              _P(stream)), "sattn_linear")
+
+
+def _rows(t: torch.Tensor, dtype, name: str) -> torch.Tensor:
+    """A 2-D view [rows, cols] with unit column stride on the GPU (leading dimensions are flattened)."""
+    if t.dtype != dtype or not t.is_cuda:
+        raise ValueError(f"{name}: expected a {dtype} CUDA tensor, got {t.dtype} on {t.device}")
+    t2 = t.view(-1, t.shape[-1]) if t.dim() != 2 else t  # a view, never a copy (outputs are written through it)
+    if t2.stride(1) != 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+    return t2
+
+
+def quantize_blocks(x: torch.Tensor):
+    """Per-block INT8 of a bf16 matrix (e.g. a linear weight [N, K]) in 128 x 128 blocks: (codes int8 [rows, cols],
+    scales float32 [ceil(rows/128), cols/128])."""
+    x2 = _rows(x, torch.bfloat16, "x")
+    rows, cols = x2.shape
+    codes = torch.empty((rows, cols), dtype=torch.int8, device=x2.device)
+    scales = torch.empty((-(-rows // SATTN_LINEAR_BLK), cols // SATTN_LINEAR_BLK if cols % SATTN_LINEAR_BLK == 0 else 1),
+                         dtype=torch.float32, device=x2.device)
+    sattn_quantize_blocks(x2.data_ptr(), rows, cols, x2.stride(0), codes.data_ptr(), scales.data_ptr(), _stream())
+    return codes, scales
+
+
+def _linear_out(x_rows: int, N: int, out, device):
+    if out is None:
+        return torch.empty((x_rows, N), dtype=torch.bfloat16, device=device)
+    o2 = _rows(out, torch.bfloat16, "out")
+    if o2.shape != (x_rows, N):
+        raise ValueError(f"out: expected {(x_rows, N)} rows x columns, got {tuple(o2.shape)}")
+    return o2
+
+
+def linear_quantized(xq: torch.Tensor, sx: torch.Tensor, wq: torch.Tensor, sw: torch.Tensor, bias=None, out=None):
+    """W8A8 linear on prepared codes (sattn_linear_quantized): y [M, N] bf16."""
+    xq2, wq2 = _rows(xq, torch.int8, "xq"), _rows(wq, torch.int8, "wq")
+    M, K = xq2.shape
+    N = wq2.shape[0]
+    if wq2.shape[1] != K or not xq2.is_contiguous() or not wq2.is_contiguous():
+        raise ValueError("xq [M, K] and wq [N, K] must be dense with the same K")
+    for t, name in ((sx, "sx"), (sw, "sw")):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name}: expected a dense float32 CUDA tensor")
+    if bias is not None and (bias.dtype != torch.bfloat16 or bias.numel() != N or not bias.is_contiguous()):
+        raise ValueError("bias: expected a dense bf16 tensor of N elements")
+    y = _linear_out(M, N, out, xq2.device)
+    sattn_linear_quantized(xq2.data_ptr(), sx.data_ptr(), wq2.data_ptr(), sw.data_ptr(),
+                           None if bias is None else bias.data_ptr(), y.data_ptr(), y.stride(0), M, N, K, _stream())
+    return y
+
+
+def linear(x: torch.Tensor, wq: torch.Tensor, sw: torch.Tensor, bias=None, mode=SATTN_LINEAR_W8A8, out=None,
+           workspace=None):
+    """The quantized linear layer y = x W^T + bias (sattn_linear) for bf16 x [..., K] and a weight prepared by
+    quantize_blocks; returns y [..., N] bf16.  mode: SATTN_LINEAR_W8A8 or SATTN_LINEAR_W8A16."""
+    x2 = _rows(x, torch.bfloat16, "x")
+    wq2 = _rows(wq, torch.int8, "wq")
+    M, K = x2.shape
+    N = wq2.shape[0]
+    if wq2.shape[1] != K or not wq2.is_contiguous():
+        raise ValueError("wq must be dense [N, K] with the K of x")
+    if sw.dtype != torch.float32 or not sw.is_cuda or not sw.is_contiguous():
+        raise ValueError("sw: expected a dense float32 CUDA tensor")
+    if bias is not None and (bias.dtype != torch.bfloat16 or bias.numel() != N or not bias.is_contiguous()):
+        raise ValueError("bias: expected a dense bf16 tensor of N elements")
+    y = _linear_out(M, N, out, x2.device)
+    need = sattn_linear_workspace_bytes(M, N, K, mode)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x2.device)
+    sattn_linear(x2.data_ptr(), x2.stride(0), wq2.data_ptr(), sw.data_ptr(), None if bias is None else bias.data_ptr(),
+                 y.data_ptr(), y.stride(0), M, N, K, mode, workspace.data_ptr(), workspace.numel(), _stream())
+    return y.view(*x.shape[:-1], N) if x.dim() != 2 else y

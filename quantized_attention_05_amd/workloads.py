@@ -190,3 +190,53 @@ def probe_layers(n_layers: int, base: Workload, seed: int = PROBE_SEED):
     factors = rng.choice(np.array([1.0, 3.0, 10.0, 30.0, 100.0]), size=n_layers)
     return [dataclasses.replace(base, name=f"{base.name}-layer{l}", dist="outlier", outlier_scale=float(f),
                                 seed=seed + 100 * l) for l, f in enumerate(factors)]
+
+
+# ---------------------------------------------------------------- quantized linear layer
+# Wan-14B linear shapes at the 720p sequence (75 600 tokens): hidden 5120, FFN 13 824.  Recipe (random numbers only):
+# x ~ N(0, 1) with 8 seeded outlier input channels scaled x20 (the channel outliers of DiT activations that make
+# per-block scales matter); W ~ N(0, 1/K); bias ~ N(0, 0.02^2).  Host draws use PCG64(seed) in the order x, outlier
+# picks, W, bias; device draws (for the full-size shapes, where values do not change the timing or the sampled
+# parity) use a torch generator seeded with the same seed.
+@dataclasses.dataclass(frozen=True)
+class LinearWorkload:
+    name: str
+    M: int
+    N: int
+    K: int
+    seed: int
+
+    @property
+    def ops(self) -> float:
+        return 2.0 * self.M * self.N * self.K
+
+
+LINEAR_WORKLOADS = {
+    "wan14b-720p-ffn-up": LinearWorkload("wan14b-720p-ffn-up", 75600, 13824, 5120, 4000),
+    "wan14b-720p-ffn-down": LinearWorkload("wan14b-720p-ffn-down", 75600, 5120, 13824, 4001),
+    "wan14b-720p-proj": LinearWorkload("wan14b-720p-proj", 75600, 5120, 5120, 4002),
+}
+LINEAR_OUTLIERS = 8
+LINEAR_OUTLIER_SCALE = 20.0
+
+
+def linear_host_inputs(M: int, N: int, K: int, seed: int, with_bias: bool = True):
+    """(x [M, K], W [N, K], bias [N] or None) as bf16 CPU tensors from PCG64(seed)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    ch = rng.choice(K, size=min(LINEAR_OUTLIERS, K), replace=False)
+    x[:, ch] *= np.float32(LINEAR_OUTLIER_SCALE)
+    w = rng.standard_normal((N, K), dtype=np.float32) * np.float32(1.0 / np.sqrt(K))
+    b = rng.standard_normal(N, dtype=np.float32) * np.float32(0.02)
+    return _to_bf16(x), _to_bf16(w), (_to_bf16(b) if with_bias else None)
+
+
+def linear_device_inputs(w: LinearWorkload, device):
+    """(x, W, bias) of a full-size linear workload drawn on the GPU (torch generator seeded with w.seed)."""
+    gen = torch.Generator(device=device).manual_seed(w.seed)
+    x = torch.randn((w.M, w.K), generator=gen, device=device)
+    ch = torch.randperm(w.K, generator=gen, device=device)[:LINEAR_OUTLIERS]
+    x[:, ch] *= LINEAR_OUTLIER_SCALE
+    wt = torch.randn((w.N, w.K), generator=gen, device=device) * (1.0 / np.sqrt(w.K))
+    b = torch.randn(w.N, generator=gen, device=device) * 0.02
+    return x.to(torch.bfloat16), wt.to(torch.bfloat16), b.to(torch.bfloat16)

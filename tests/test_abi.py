@@ -142,6 +142,35 @@ def test_argument_errors_are_caught_on_the_host(S):
     assert es(byref(o96), byref(o96), ctypes.c_void_p(P), None) == S.SATTN_ERR_UNSUPPORTED
     many = _t(S, P, 1, 65536, 1, 64)
     assert es(byref(many), byref(many), ctypes.c_void_p(P), None) == S.SATTN_ERR_UNSUPPORTED
+    # quantized linear layer: every call below stops at a host check (the pointers are fake)
+    vp = ctypes.c_void_p
+    qb = L.sattn_quantize_blocks
+    assert qb(vp(P), 256, 100, 128, vp(P), vp(P), None) == S.SATTN_ERR_UNSUPPORTED       # cols not a multiple of 128
+    assert qb(vp(P), 0, 128, 128, vp(P), vp(P), None) == S.SATTN_ERR_INVALID_ARG          # no rows
+    assert qb(vp(P + 2), 256, 128, 128, vp(P), vp(P), None) == S.SATTN_ERR_INVALID_ARG    # misaligned x
+    assert qb(vp(P), 256, 128, 120, vp(P), vp(P), None) == S.SATTN_ERR_INVALID_ARG        # ld < cols
+    assert qb(None, 256, 128, 128, vp(P), vp(P), None) == S.SATTN_ERR_INVALID_ARG
+    lq = L.sattn_linear_quantized
+    assert lq(vp(P), vp(P), vp(P), vp(P), None, vp(P), 256, 256, 256, 100, None) == S.SATTN_ERR_UNSUPPORTED  # K
+    assert lq(vp(P), vp(P), vp(P), vp(P), None, vp(P), 248, 256, 256, 128, None) == S.SATTN_ERR_INVALID_ARG  # ldy < N
+    assert lq(vp(P), vp(P), vp(P), vp(P), None, vp(P + 1), 256, 256, 256, 128, None) == S.SATTN_ERR_INVALID_ARG
+    assert lq(None, vp(P), vp(P), vp(P), None, vp(P), 256, 256, 256, 128, None) == S.SATTN_ERR_INVALID_ARG
+    big = 1 << 28  # (2^21)^2 output tiles
+    assert lq(vp(P), vp(P), vp(P), vp(P), None, vp(P), big, big, big, 128, None) == S.SATTN_ERR_UNSUPPORTED
+    ln = L.sattn_linear
+    need = L.sattn_linear_workspace_bytes(256, 300, 256, 0)
+    assert need == 65536 + 256 and L.sattn_linear_workspace_bytes(256, 300, 256, 1) == 300 * 256 * 2
+    assert L.sattn_linear_workspace_bytes(256, 300, 100, 0) == 0 and L.sattn_linear_workspace_bytes(256, 300, 256, 7) == 0
+
+    def lin(mode=0, ws=P, ws_bytes=need, ldx=256):
+        return ln(vp(P), ldx, vp(P), vp(P), None, vp(P), 304, 256, 300, 256, mode, vp(ws) if ws else None, ws_bytes,
+                  None)
+    assert lin(mode=5) == S.SATTN_ERR_INVALID_ARG
+    assert lin(ws=0) == S.SATTN_ERR_WORKSPACE
+    assert lin(ws_bytes=need - 1) == S.SATTN_ERR_WORKSPACE
+    assert lin(ws=P + 16) == S.SATTN_ERR_INVALID_ARG           # workspace not 256-byte aligned
+    assert lin(ldx=252) == S.SATTN_ERR_INVALID_ARG             # ldx < K
+    assert lin(ldx=1 << 23) == S.SATTN_ERR_UNSUPPORTED         # a 128-row tile of x would span 2^31 bytes
     # cross-attention and the quantized entry points validate the same way
     assert L.sattn_cross_fwd(byref(q), byref(k), byref(v), byref(o), 0.0, 2, None, 0, None) == S.SATTN_ERR_WORKSPACE
     assert L.sattn_fwd_quantized(None, None, None, byref(o), 0.0, 2, None) == S.SATTN_ERR_INVALID_ARG
