@@ -12,8 +12,8 @@
 //                         2 x 2 blocks of 32 x 32 on the matrix cores (v_mfma_i32_32x32x32_i8, or
 //                         v_mfma_f32_32x32x16_bf16).  The matrix cores accumulate one K block exactly (int32) or in
 //                         fp32; at its end the partial sums are scaled and added to the fp32 accumulators.
-//                         Operands stream through a 4-stage LDS ring of 64-byte row slices with direct-to-LDS
-//                         buffer loads three stages ahead.
+//                         Operands stream through a 2-stage LDS ring of 128-byte row slices (direct-to-LDS
+//                         buffer loads, one stage ahead); the fold of one K block overlaps the next one's matrix ops.
 #include <algorithm>
 #include <type_traits>
 
@@ -105,26 +105,35 @@ __global__ void __launch_bounds__(kLinThreads) codes_to_bf16_kernel(const int8_t
 
 // ---------------------------------------------------------------------------------------------------------
 // The GEMM.
+constexpr int kLinRow = 128;  // bytes of one operand row per LDS stage
+constexpr int kLinRing = 2;   // LDS ring stages
+
 template <bool A8>
 struct LinGeo {
   static constexpr int EB = A8 ? 1 : 2;           // bytes per operand element
-  static constexpr int ROW = 64;                  // bytes of one operand row per stage (4 granules of 16 B)
-  static constexpr int SPB = kLinBlk * EB / ROW;  // stages per 128-wide K block: 2 (INT8) or 4 (bf16)
+  static constexpr int ROW = kLinRow;             // bytes of one operand row per stage (granules of 16 B)
+  static constexpr int G16 = ROW / 16;            // granules per row
+  static constexpr int SPB = kLinBlk * EB / ROW;  // stages per 128-wide K block
   static constexpr int KSTEPS = ROW / 32;         // matrix-core k-steps per stage, 32 bytes of K each
-  static constexpr int TILE = kLinBlk * ROW;      // one operand slice: 128 rows x 64 B = 8 KiB
+  static constexpr int TILE = kLinBlk * ROW;      // one operand slice: 128 rows x ROW bytes
   static constexpr int STAGE = 2 * TILE;          // activations + weights
-  static constexpr int R = 4;                     // ring stages
-  static constexpr int DIST = R - 1;              // a stage is loaded this many iterations before its use
+  static constexpr int R = kLinRing;              // ring stages
+  static constexpr int DIST = R - 1;              // a stage is loaded this many stages ahead of its use
   static constexpr int LPT = TILE / (16 * kLinThreads);  // 16-byte loads per thread per slice
   static constexpr int OPS = 2 * LPT;                    // loads per thread per stage
-  static constexpr int BYTES = R * STAGE;                // 64 KiB; the per-K-block scale list follows
+  static constexpr int BYTES = R * STAGE;                // the per-K-block scale list follows
   static_assert(LPT * 16 * kLinThreads == TILE, "slices split into whole loads");
+  static_assert(R % SPB == 0 || SPB % R == 0, "ring slots follow the unrolled stages");
 };
 
-// XOR swizzle of the 4 granules of a 64-byte LDS row.  The 16 lanes of a quarter-wave read 16 consecutive rows at one
-// logical granule (and the 8 lanes of an eighth, 8 rows); this map sends them to distinct bank groups for 64 and for
-// 32 LDS banks.
-__device__ __forceinline__ int lswz(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+// XOR swizzles of the 16-byte granules of an LDS row (4 or 8 granules).  The 16 lanes of a quarter-wave read 16
+// consecutive rows at one logical granule (and the 8 lanes of an eighth, 8 rows); these maps send them to distinct
+// bank groups for 64 and for 32 LDS banks.
+template <int G16>
+__device__ __forceinline__ int lswz(int row) {
+  if (G16 == 4) return ((row >> 1) & 3) ^ ((row >> 3) & 1);
+  return ((row >> 1) & 7) ^ ((row & 1) << 2);
+}
 
 // Workgroups are handed to the 8 XCDs round-robin; renumber them so that each XCD gets one contiguous range.
 __device__ __forceinline__ int xcd_order(int wg, int nwg) {
@@ -137,7 +146,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
 
+// Workgroup barrier of the K loop.  The slot of the previous stage is refilled right after it, so every LDS read this
+// wave issued must have returned first: the compiler may place the wait for a read's data (at its first use) after
+// the barrier, hence the explicit lgkmcnt(0).  The wavefront-scope fences keep the compiler from moving LDS accesses
+// across the barrier; without a workgroup fence the barrier does not wait for the tile loads in flight.
 __device__ __forceinline__ void ring_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -150,15 +164,19 @@ __device__ __forceinline__ v16f mma_bf16(const v8bf& a, const v8bf& b, const v16
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// The K loop runs stage by stage: wait for the stage, barrier, load the next stage into the other slot, run the
+// stage's k-steps on the matrix cores.  The partial sums of consecutive K blocks alternate between two register
+// sets, so the scaled fold of K block kb - 1 into the fp32 accumulators is independent of the matrix ops of K block
+// kb and sits in the same scheduling region: the vector ALU works while the matrix cores run.
 template <bool A8>
 __global__ void __launch_bounds__(kLinThreads, 2) linear_kernel(LinearArg p) {
   // (the body is device code only: the host pass needs just the signature for the launch stub, and it would drop the
   // stub over the target builtins and register constraints below)
 #if defined(__HIP_DEVICE_COMPILE__)
   using G = LinGeo<A8>;
-  using Part = std::conditional_t<A8, v16i, v16f>;  // one K block's partial sums
+  using Part = std::conditional_t<A8, v16i, v16f>;  // one K block's partial sums of a 32 x 32 block
   using Opnd = std::conditional_t<A8, v4i, v8bf>;
-  constexpr int R = G::R, DIST = G::DIST;
+  constexpr int R = G::R;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int lane = threadIdx.x & 63;
@@ -185,28 +203,38 @@ __global__ void __launch_bounds__(kLinThreads, 2) linear_kernel(LinearArg p) {
     cs[kb] = A8 ? p.sx[(int64_t)mt * nkb + kb] * p.sw[(int64_t)nt * nkb + kb] : p.sw[(int64_t)nt * nkb + kb];
   __syncthreads();  // a full workgroup barrier: the list is written with ordinary LDS stores (no tile load in flight yet)
 
-  // buffers over the tile's rows: rows past M (N) lie past the buffer end and read as zero
+  // the tile's rows; a stage reads them through a buffer that starts at its K offset and ends after the last row in
+  // the matrix, so rows past M (N) read as zero
   const int arows = min(kLinBlk, p.M - m0), brows = min(kLinBlk, p.N - n0);
-  const auto ra = rows_rsrc(p.a + (int64_t)m0 * p.lda, arows * (int)p.lda);
-  const auto rb = rows_rsrc(p.b + (int64_t)n0 * p.ldb, brows * (int)p.ldb);
+  const uint8_t* abase = p.a + (int64_t)m0 * p.lda;
+  const uint8_t* bbase = p.b + (int64_t)n0 * p.ldb;
+  const int abytes = arows * (int)p.lda, bbytes = brows * (int)p.ldb;
   // load plan: load j of this wave fills LDS granules [(4 j + wave) * 64, +64) of a slice; LDS granule q holds row
-  // q / 4, logical granule (q % 4) ^ lswz(row)
+  // q / G16, logical granule (q % G16) ^ lswz(row).  The K offset of a stage goes in the buffer base.
+  constexpr int G16 = G::G16;
   int la[G::LPT], lb[G::LPT];
 #pragma unroll
   for (int j = 0; j < G::LPT; ++j) {
     const int q = (4 * j + wave) * 64 + lane;
-    const int row = q >> 2, lg = (q & 3) ^ lswz(row);
+    const int row = q / G16, lg = (q % G16) ^ lswz<G16>(row);
     la[j] = row * (int)p.lda + 16 * lg;
     lb[j] = row * (int)p.ldb + 16 * lg;
   }
-  auto issue = [&](int t) {
-    uint8_t* st = smem + (t % R) * G::STAGE;
-    const int kbyte = t * G::ROW;
+  const int T = nkb * G::SPB;  // stages
+  // loads of stage t's data (clamped to the last stage: the tail reloads it into a free slot, so that no branch
+  // splits the loop body) into ring slot SLOT
+  auto issue = [&](int t, auto slot_tag) __attribute__((always_inline)) {
+    constexpr int SLOT = decltype(slot_tag)::value;
+    uint8_t* st = smem + SLOT * G::STAGE;
+    const int kbyte = min(t, T - 1) * G::ROW;
+    // (a row's bytes from kbyte on stay inside the buffer: kbyte + ROW <= K * EB <= ld)
+    const auto ra = rows_rsrc(abase + kbyte, abytes - kbyte);
+    const auto rb = rows_rsrc(bbase + kbyte, bbytes - kbyte);
 #pragma unroll
     for (int j = 0; j < G::LPT; ++j) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(st + (4 * j + wave) * 1024), 16, la[j] + kbyte, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(st + G::TILE + (4 * j + wave) * 1024), 16,
-                                               lb[j] + kbyte, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(st + (4 * j + wave) * 1024), 16, la[j], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(st + G::TILE + (4 * j + wave) * 1024), 16, lb[j], 0,
+                                               0, 0);
     }
   };
   // operand reads: 32-row block i of this wave, k-step s: row (64 w + 32 i + lane % 32), logical granule 2 s + lane / 32
@@ -216,13 +244,13 @@ __global__ void __launch_bounds__(kLinThreads, 2) linear_kernel(LinearArg p) {
     const int arow = 64 * wm + 32 * i + n32, brow = 64 * wn + 32 * i + n32;
 #pragma unroll
     for (int s = 0; s < G::KSTEPS; ++s) {
-      ard[i][s] = arow * G::ROW + 16 * ((2 * s + g) ^ lswz(arow));
-      brd[i][s] = G::TILE + brow * G::ROW + 16 * ((2 * s + g) ^ lswz(brow));
+      ard[i][s] = arow * G::ROW + 16 * ((2 * s + g) ^ lswz<G16>(arow));
+      brd[i][s] = G::TILE + brow * G::ROW + 16 * ((2 * s + g) ^ lswz<G16>(brow));
     }
   }
 
   v16f acc[2][2];
-  Part part[2][2];
+  Part part[2][2][2];  // [register set][i][j]
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -230,22 +258,29 @@ __global__ void __launch_bounds__(kLinThreads, 2) linear_kernel(LinearArg p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int T = p.K * G::EB / G::ROW;  // stages (at least SPB >= 2)
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  // fold rows-block range [I0, I1) of register set SET (scale factor fc) into the accumulators
+  auto fold = [&](float fc, auto set_tag, auto i0_tag, auto i1_tag) __attribute__((always_inline)) {
+    constexpr int SET = decltype(set_tag)::value, I0 = decltype(i0_tag)::value, I1 = decltype(i1_tag)::value;
 #pragma unroll
-  for (int t = 0; t < DIST; ++t)
-    if (t < T) issue(t);
-
-  // one stage: wait for it, release the slot of stage t + DIST, and run its k-steps on the matrix cores; FRESH (the
-  // first stage of a K block) starts the partial sums from zero
-  auto stage = [&](int t, auto fresh_tag) __attribute__((always_inline)) {
+    for (int i = I0; i < I1; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(fc, (float)part[SET][i][j][r], acc[i][j][r]);
+  };
+  // stage t (ring slot SLOT) into register set SET: wait until the stage has landed for every wave, refill the slot
+  // of stage t - 1 with stage t + DIST, run the k-steps (FRESH: the first stage of a K block, from zero), and fold
+  // the part [FI0, FI1) of the other register set (the previous K block, scale factor fc)
+  auto stage = [&](int t, auto slot_tag, auto set_tag, auto fresh_tag, auto fi0_tag, auto fi1_tag, float fc)
+      __attribute__((always_inline)) {
+    constexpr int SLOT = decltype(slot_tag)::value, SET = decltype(set_tag)::value;
     constexpr bool FRESH = decltype(fresh_tag)::value;
-    // stage t has landed for every wave once each has waited for its own loads of it
-    if (t + DIST - 1 < T) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DIST - 1) * G::OPS) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    ring_sync();
-    // the slot of stage t + DIST was last read in iteration t - 1, which every wave has finished
-    if (t + DIST < T) issue(t + DIST);
-    const uint8_t* st = smem + (t % R) * G::STAGE;
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((G::DIST - 1) * G::OPS) : "memory");  // this wave's loads of stage t
+    ring_sync();  // ... and every other wave's; all reads of stage t - 1 are done, so its slot can be refilled
+    issue(t + G::DIST, std::integral_constant<int, (SLOT + G::DIST) % R>{});
+    const uint8_t* st = smem + SLOT * G::STAGE;
 #pragma unroll
     for (int s = 0; s < G::KSTEPS; ++s) {
       Opnd av[2], bv[2];
@@ -258,32 +293,79 @@ __global__ void __launch_bounds__(kLinThreads, 2) linear_kernel(LinearArg p) {
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          Part c0 = part[i][j];
+          Part c0 = part[SET][i][j];
           if (FRESH && s == 0) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) c0[r] = 0;
           }
-          if constexpr (A8) part[i][j] = mma_i8(av[i], bv[j], c0);
-          else part[i][j] = mma_bf16(av[i], bv[j], c0);
+          if constexpr (A8) part[SET][i][j] = mma_i8(av[i], bv[j], c0);
+          else part[SET][i][j] = mma_bf16(av[i], bv[j], c0);
         }
     }
+    fold(fc, std::integral_constant<int, SET ^ 1>{}, fi0_tag, fi1_tag);
   };
-  for (int kb = 0; kb < nkb; ++kb) {
-    stage(kb * G::SPB, std::true_type{});
+  // one K block whose first stage sits in ring slot SLOT0, into register set SET; with FOLD, the previous K block
+  // (other set) is folded in halves over the first two stages (INT8) or all at once in the first (one stage)
+  auto kblock = [&](int kb, auto slot0_tag, auto set_tag, auto fold_tag) __attribute__((always_inline)) {
+    constexpr int SLOT0 = decltype(slot0_tag)::value;
+    constexpr bool FOLD = decltype(fold_tag)::value;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, FOLD ? (G::SPB >= 2 ? 1 : 2) : 0>;
+    using I2 = std::integral_constant<int, FOLD ? 2 : 0>;
+    const float fc = FOLD ? cs[kb - 1] : 0.0f;
+    stage(kb * G::SPB, slot0_tag, set_tag, std::true_type{}, I0{}, I1{}, fc);
 #pragma unroll
-    for (int u = 1; u < G::SPB; ++u) stage(kb * G::SPB + u, std::false_type{});
-    const float c = cs[kb];  // end of the K block: acc += c * partial
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(c, (float)part[i][j][r], acc[i][j][r]);
+    for (int u = 1; u < G::SPB; ++u) {
+      // (u is a compile-time constant after unrolling; the slot and the fold range follow from it)
+      if (u == 1)
+        stage(kb * G::SPB + 1, std::integral_constant<int, (SLOT0 + 1) % R>{}, set_tag, std::false_type{}, I1{},
+              I2{}, fc);
+      else if (u == 2)
+        stage(kb * G::SPB + 2, std::integral_constant<int, (SLOT0 + 2) % R>{}, set_tag, std::false_type{}, I0{},
+              I0{}, 0.0f);
+      else
+        stage(kb * G::SPB + 3, std::integral_constant<int, (SLOT0 + 3) % R>{}, set_tag, std::false_type{}, I0{},
+              I0{}, 0.0f);
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I2 = std::integral_constant<int, 2>;
+  // prologue: stages 0 .. DIST-1 (clamped) into slots 0 .. DIST-1
+  issue(0, S0{});
+  if constexpr (G::DIST > 1) issue(1, S1{});
+  if constexpr (G::DIST > 2) issue(2, std::integral_constant<int, 2>{});
+  static_assert(G::DIST <= 3, "the prologue issues DIST stages");
+  constexpr int KSLOTS = (G::SPB * 2) % R;  // slot advance over two K blocks
+  static_assert(KSLOTS == 0, "two K blocks fill the ring a whole number of times");
+  if constexpr (A8) {
+    // INT8: the fold costs as much vector work as a K block's matrix ops; two register sets overlap them
+    kblock(0, S0{}, S0{}, std::false_type{});
+    int kb = 1;
+    constexpr int SLOT_ODD = G::SPB % R;  // first slot of an odd K block
+    for (; kb + 1 < nkb; kb += 2) {
+      kblock(kb, std::integral_constant<int, SLOT_ODD>{}, S1{}, std::true_type{});
+      kblock(kb + 1, S0{}, S0{}, std::true_type{});
+    }
+    if (kb < nkb) {  // nkb even: the last K block (odd) goes to set 1
+      kblock(kb, std::integral_constant<int, SLOT_ODD>{}, S1{}, std::true_type{});
+      fold(cs[nkb - 1], S1{}, I0{}, I2{});
+    } else {
+      fold(cs[nkb - 1], S0{}, I0{}, I2{});
+    }
+  } else {
+    // bf16: four times the matrix work per fold and one register set (two would not fit with the wider operands);
+    // every K block fills the ring exactly, so each starts in slot 0
+    static_assert(G::SPB % R == 0, "a bf16 K block starts in slot 0");
+    for (int kb = 0; kb < nkb; ++kb) {
+      kblock(kb, S0{}, S1{}, std::false_type{});
+      fold(cs[kb], S1{}, I0{}, I2{});
+    }
   }
 
-  // epilogue through LDS (the ring is free once every wave is past its last stage): the wave writes its 64 x 64
-  // block as bf16 rows of 128 bytes, then stores them 16 bytes per lane.  Lane holds column 32 j + lane % 32 of the
-  // block; register r of block i is row 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4.
+  // epilogue through LDS (the ring is free once every wave is past its last stage and the extra load of the last
+  // stage has landed): the wave writes its 64 x 64 block as bf16 rows of 128 bytes, then stores them 16 bytes per
+  // lane.  Lane holds column 32 j + lane % 32 of the block; register r of block i is row
+  // 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   uint16_t* ot = reinterpret_cast<uint16_t*>(smem) + wave * 64 * 64;
