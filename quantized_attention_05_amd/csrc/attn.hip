@@ -117,10 +117,12 @@ __device__ __forceinline__ void lds_load4_buf(__amdgpu_buffer_rsrc_t r, int voff
 }
 // Workgroup barrier of the pipelined loop, without the memory-model waits of __syncthreads (whose workgroup
 // release would wait for every tile load in flight).  Inside the loop LDS is written only by the tile loads,
-// which each wave waits for explicitly (vmcnt) before the barrier, and every LDS read of a stage completes before
-// the barrier that precedes its overwrite; the wavefront-scope fences only stop the compiler from moving LDS
-// accesses across the barrier.
+// which each wave waits for explicitly (vmcnt) before the barrier.  Every LDS read of a stage must have returned
+// before the barrier that precedes its overwrite: the compiler may place the wait for a read's data (at its first
+// use) after the barrier, hence the explicit lgkmcnt(0).  The wavefront-scope fences only stop the compiler from
+// moving LDS accesses across the barrier.
 __device__ __forceinline__ void ring_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
