@@ -186,9 +186,9 @@ __global__ void __launch_bounds__(kLinThreads, 2) linear_kernel(LinearArg p) {
   const int mtiles = (p.M + kLinBlk - 1) / kLinBlk, ntiles = (p.N + kLinBlk - 1) / kLinBlk;
   const int nkb = p.K / kLinBlk;
 
-  // output tile: XCD-contiguous ranges, then groups of 8 row tiles walked column tile by column tile, so the
+  // output tile: XCD-contiguous ranges, then groups of 4 row tiles walked column tile by column tile, so the
   // workgroups that run together share both their activation and their weight slices in L2
-  constexpr int GM = 8;
+  constexpr int GM = 4;
   const int logical = xcd_order(blockIdx.x, gridDim.x);
   const int grp = logical / (GM * ntiles);
   const int first = grp * GM;
