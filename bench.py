@@ -151,7 +151,8 @@ def block_sparse(args):
         "value": round(ops_kept / (ms * 1e-3) / 1e12, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": MODE_DTYPE[mode],
-        "data": "synthetic: N(0,1) drawn on the GPU; band block mask (recipe in DESIGN.md)",
+        "data": ("synthetic: N(0,1) drawn on the GPU; band block mask "
+                 "(recipe in quantized_attention_05_amd/workloads.py)"),
         "config": {"workload": "wan14b-720p block-sparse self-attention", "B": w.B, "H": w.H, "Nq": w.Nq,
                    "Nkv": w.Nkv, "d": w.d, "mode": wl.MODE_NAMES[mode], "mask": "band, half-width 9450 tokens, 1 sink",
                    "kept_block_fraction": round(float(mask_np.mean()), 4),
@@ -255,7 +256,7 @@ def linear_layers(args):
             "value": tops(ms8), "unit": "TOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(ms8, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "int8 (W8A8, 128x128 blocks)", "data": "synthetic: N(0,1) x with x20 outlier channels, "
-            "N(0,1/K) weights, drawn on the GPU (recipe in DESIGN.md)",
+            "N(0,1/K) weights, drawn on the GPU (recipe in quantized_attention_05_amd/workloads.py)",
             "config": {"workload": f"{name} linear", "M": w.M, "N": w.N, "K": w.K},
             "pct_int8_mfma_peak": round(100 * w.ops / (ms8 * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2),
             "w8a8_ms": round(ms8, 4), "w8a16_ms": round(ms16, 4), "w8a16_tops": tops(ms16),
@@ -442,7 +443,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": MODE_DTYPE[mode],
-        "data": "synthetic: seeded Wan-shaped N(0,1) Q/K/V, K per-channel offsets, zeroed K blocks (recipe in DESIGN.md)",
+        "data": ("synthetic: seeded Wan-shaped N(0,1) Q/K/V, K per-channel offsets, zeroed K blocks "
+                 "(recipe in quantized_attention_05_amd/workloads.py)"),
         "config": {"workload": f"{w.name} self-attention" if "cross" not in w.name else f"{w.name} attention",
                    "B": w.B, "H": w.H, "Nq": w.Nq, "Nkv": w.Nkv, "d": w.d, "mode": wl.MODE_NAMES[mode],
                    "blk_q": w.blk_q, "blk_k": w.blk_k, "parallelism": "single GPU"},

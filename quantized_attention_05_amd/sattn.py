@@ -349,8 +349,8 @@ def quantize_blocks(x: torch.Tensor):
     x2 = _rows(x, torch.bfloat16, "x")
     rows, cols = x2.shape
     codes = torch.empty((rows, cols), dtype=torch.int8, device=x2.device)
-    scales = torch.empty((-(-rows // SATTN_LINEAR_BLK), cols // SATTN_LINEAR_BLK if cols % SATTN_LINEAR_BLK == 0 else 1),
-                         dtype=torch.float32, device=x2.device)
+    nbc = cols // SATTN_LINEAR_BLK if cols % SATTN_LINEAR_BLK == 0 else 1  # (other widths are refused by the call)
+    scales = torch.empty((-(-rows // SATTN_LINEAR_BLK), nbc), dtype=torch.float32, device=x2.device)
     sattn_quantize_blocks(x2.data_ptr(), rows, cols, x2.stride(0), codes.data_ptr(), scales.data_ptr(), _stream())
     return codes, scales
 

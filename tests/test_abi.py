@@ -160,7 +160,8 @@ def test_argument_errors_are_caught_on_the_host(S):
     ln = L.sattn_linear
     need = L.sattn_linear_workspace_bytes(256, 300, 256, 0)
     assert need == 65536 + 256 and L.sattn_linear_workspace_bytes(256, 300, 256, 1) == 300 * 256 * 2
-    assert L.sattn_linear_workspace_bytes(256, 300, 100, 0) == 0 and L.sattn_linear_workspace_bytes(256, 300, 256, 7) == 0
+    assert L.sattn_linear_workspace_bytes(256, 300, 100, 0) == 0
+    assert L.sattn_linear_workspace_bytes(256, 300, 256, 7) == 0
 
     def lin(mode=0, ws=P, ws_bytes=need, ldx=256):
         return ln(vp(P), ldx, vp(P), vp(P), None, vp(P), 304, 256, 300, 256, mode, vp(ws) if ws else None, ws_bytes,

@@ -1,6 +1,6 @@
 """GPU parity of the quantized linear layer (sattn_quantize_blocks, sattn_linear_quantized, sattn_linear through the
-C ABI) with the CPU oracle (TMAP I2V write-up, section "FFN性能优化 / 线性层量化": 8-bit weights in 128 x 128 blocks,
-W8A8 with a W8A16 fallback).
+C ABI) with the CPU oracle (TMAP I2V write-up, section "FFN性能优化 / 线性层量化": 8-bit weights in 128 x 128
+blocks, W8A8 with a W8A16 fallback).
 
 * Codes and block scales are integer decisions: bit-exact against the oracle.
 * Outputs are compared with the oracle's fp64 value y.  The kernels multiply exactly (int32 per K block in W8A8;
