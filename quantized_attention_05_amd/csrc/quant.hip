@@ -129,36 +129,42 @@ __global__ void __launch_bounds__(256) kv_stats_kernel(TensorArg k, TensorArg v,
   }
 }
 
-// One thread per (b, h, c): run sums added in run order -> mean; V maxima -> scale and reciprocal.
+// Threads [0, B*H*d): one per (b, h, c), run sums added in run order -> K mean.  Threads [B*H*d, 2*B*H*d) (with V):
+// one per (b, h, c), V maxima -> scale and reciprocal.  Both are bound by the latency of their loads, so 64 are
+// issued together; the K additions stay one after another in run order.
 __global__ void __launch_bounds__(128) kv_finalize_kernel(QuantArg qa, bool with_v, const float* ksum, const float* vmax,
                                                           float* vinv) {
+  constexpr int kBatch = 64;
   const int d = qa.d;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)qa.B * qa.H * d) return;
+  const int64_t n = (int64_t)qa.B * qa.H * d;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool vpart = i >= n;
+  if (vpart) i -= n;
+  if (i >= n || (vpart && !with_v)) return;
   const int64_t bh = i / d;
   const int c = (int)(i % d);
-  const float* ps = ksum + bh * qa.nkb * d + c;
-  float total = 0.0f;
   int r = 0;
-  // the loads of 16 run sums are issued together; the additions stay one after another in run order
-  for (; r + 16 <= qa.nkb; r += 16) {
-    float x[16];
+  if (!vpart) {
+    const float* ps = ksum + bh * qa.nkb * d + c;
+    float total = 0.0f;
+    for (; r + kBatch <= qa.nkb; r += kBatch) {
+      float x[kBatch];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) x[u] = ps[(int64_t)(r + u) * d];
+      for (int u = 0; u < kBatch; ++u) x[u] = ps[(int64_t)(r + u) * d];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) total = total + x[u];
-  }
-  for (; r < qa.nkb; ++r) total = total + ps[(int64_t)r * d];
-  qa.k_mean[i] = total / (float)qa.Nkv;
-  if (with_v) {
+      for (int u = 0; u < kBatch; ++u) total = total + x[u];
+    }
+    for (; r < qa.nkb; ++r) total = total + ps[(int64_t)r * d];
+    qa.k_mean[i] = total / (float)qa.Nkv;
+  } else {
     const float* pm = vmax + bh * qa.nkb * d + c;
     float a = 0.0f;
-    for (r = 0; r + 16 <= qa.nkb; r += 16) {
-      float x[16];
+    for (; r + kBatch <= qa.nkb; r += kBatch) {
+      float x[kBatch];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) x[u] = pm[(int64_t)(r + u) * d];
+      for (int u = 0; u < kBatch; ++u) x[u] = pm[(int64_t)(r + u) * d];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) a = fmaxf(a, x[u]);
+      for (int u = 0; u < kBatch; ++u) a = fmaxf(a, x[u]);
     }
     for (; r < qa.nkb; ++r) a = fmaxf(a, pm[(int64_t)r * d]);
     const bool zero = !(a >= kGuard);
@@ -295,7 +301,7 @@ hipError_t launch_kv_stats(const TensorArg& k, const TensorArg& v, bool with_v, 
 
 hipError_t launch_kv_finalize(const QuantArg& qa, bool with_v, const float* ksum, const float* vmax, float* vinv,
                               hipStream_t s) {
-  const int64_t n = (int64_t)qa.B * qa.H * qa.d;
+  const int64_t n = (int64_t)qa.B * qa.H * qa.d * (with_v ? 2 : 1);
   kv_finalize_kernel<<<(unsigned)((n + 127) / 128), 128, 0, s>>>(qa, with_v, ksum, vmax, vinv);
   return hipGetLastError();
 }
