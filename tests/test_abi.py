@@ -188,3 +188,18 @@ def test_binding_raises(S):
     with pytest.raises(S.SattnError) as ei:
         S.sattn_fwd(None, None, None, None, 0.0, 2, 64, 64, 0, 0, 0)
     assert ei.value.status == S.SATTN_ERR_INVALID_ARG
+
+
+def test_linear_binding_validates_before_the_call(S):
+    """The torch-level linear entry points raise ValueError for host tensors and wrong dtypes before any C call (the
+    checks that need device tensors, shapes and strides, are exercised by the GPU tests)."""
+    import torch
+
+    x = torch.zeros((4, 128), dtype=torch.bfloat16)
+    wq = torch.zeros((8, 128), dtype=torch.int8)
+    sw = torch.zeros((1, 1), dtype=torch.float32)
+    for call in (lambda: S.quantize_blocks(x), lambda: S.quantize_blocks(x.float()),
+                 lambda: S.linear(x, wq, sw), lambda: S.linear(x.to(torch.float16), wq, sw),
+                 lambda: S.linear_quantized(wq, sw, wq.to(torch.int16), sw)):
+        with pytest.raises(ValueError):
+            call()
