@@ -11,7 +11,9 @@
 //                         workgroup: s_x s_w (W8A8) or s_w (W8A16).  Four waves each own 64 x 64 of the tile as
 //                         2 x 2 blocks of 32 x 32 on the matrix cores (v_mfma_i32_32x32x32_i8, or
 //                         v_mfma_f32_32x32x16_bf16).  The matrix cores accumulate one K block exactly (int32) or in
-//                         fp32; at its end the partial sums are scaled and added to the fp32 accumulators.
+//                         fp32; at its end the partial sums are scaled and added to the fp32 accumulators (INT8: the
+//                         int32 sums start from a float's bit pattern, so that one exact subtraction replaces the
+//                         int-to-float conversion).
 //                         Operands stream through a 2-stage LDS ring of 128-byte row slices (direct-to-LDS
 //                         buffer loads, one stage ahead); the fold of one K block overlaps the next one's matrix ops.
 #include <algorithm>
@@ -106,6 +108,16 @@ __global__ void __launch_bounds__(kLinThreads) codes_to_bf16_kernel(const int8_t
 // ---------------------------------------------------------------------------------------------------------
 // The GEMM.
 constexpr int kLinRow = 128;  // bytes of one operand row per LDS stage
+
+// The INT8 partial sums of a K block start from the bit pattern of the float 1/(2 pi) (an inline constant of the
+// matrix-core instruction).  A K block's sum obeys |S| <= 128 * 127^2 < 2^21, and adding S to that pattern stays in
+// the binade [2^-3, 2^-2), whose spacing is 2^-26: read as a float the result is 1/(2 pi) + S 2^-26 exactly, and
+// subtracting 1/(2 pi) gives S 2^-26 exactly (Sterbenz).  The fp32 accumulators therefore hold y 2^-26, and the
+// epilogue scales them back by 2^26 exactly.  Every rounding is the one of the unscaled sum while the scaled values
+// stay normal (|y| above about 2^-100).
+[[maybe_unused]] constexpr int kI8Bias = 0x3E22F983;
+[[maybe_unused]] constexpr float kI8BiasF = 0.15915494309189535f;  // the float with those bits
+[[maybe_unused]] constexpr float kI8Unit = 67108864.0f;            // 2^26
 constexpr int kLinRing = 2;   // LDS ring stages
 
 template <bool A8>
@@ -268,7 +280,12 @@ __global__ void __launch_bounds__(kLinThreads, 2) linear_kernel(LinearArg p) {
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(fc, (float)part[SET][i][j][r], acc[i][j][r]);
+        for (int r = 0; r < 16; ++r) {
+          if constexpr (A8)
+            acc[i][j][r] = __builtin_fmaf(fc, __int_as_float(part[SET][i][j][r]) - kI8BiasF, acc[i][j][r]);
+          else
+            acc[i][j][r] = __builtin_fmaf(fc, part[SET][i][j][r], acc[i][j][r]);
+        }
   };
   // stage t (ring slot SLOT) into register set SET: wait until the stage has landed for every wave, refill the slot
   // of stage t - 1 with stage t + DIST, run the k-steps (FRESH: the first stage of a K block, from zero), and fold
@@ -296,7 +313,10 @@ __global__ void __launch_bounds__(kLinThreads, 2) linear_kernel(LinearArg p) {
           Part c0 = part[SET][i][j];
           if (FRESH && s == 0) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) c0[r] = 0;
+            for (int r = 0; r < 16; ++r) {
+              if constexpr (A8) c0[r] = kI8Bias;
+              else c0[r] = 0.0f;
+            }
           }
           if constexpr (A8) part[SET][i][j] = mma_i8(av[i], bv[j], c0);
           else part[SET][i][j] = mma_bf16(av[i], bv[j], c0);
@@ -379,7 +399,7 @@ __global__ void __launch_bounds__(kLinThreads, 2) linear_kernel(LinearArg p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int rl = 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
-        const __bf16 h = (__bf16)(acc[i][j][r] + bias);
+        const __bf16 h = (__bf16)(A8 ? __builtin_fmaf(acc[i][j][r], kI8Unit, bias) : acc[i][j][r] + bias);
         ot[rl * 64 + cl] = __builtin_bit_cast(uint16_t, h);
       }
   }
