@@ -6,17 +6,20 @@
 //   quant_blocks_kernel   one workgroup per 128 x 128 block of a bf16 matrix: block max, INT8 codes, block scale
 //                         (the symmetric rule of the attention blocks: scale a/127, codes rint(v * 127/a)).
 //   codes_to_bf16_kernel  INT8 codes to bf16 (exact: |code| <= 127 needs 7 bits), the W8A16 weight operand.
-//   linear_kernel<A8>     the GEMM.  A workgroup owns one 128 x 128 output tile, which is exactly one (row block,
-//                         column block) pair of scale blocks, so every 128-wide K block has one scale factor per
-//                         workgroup: s_x s_w (W8A8) or s_w (W8A16).  Four waves each own 64 x 64 of the tile as
+//   linear_kernel<A8,WR>  the GEMM.  A workgroup owns a (64 WR) x 128 output tile: 128 x 128 with 4 waves (W8A8, and
+//                         W8A16 on one row block) or 256 x 128 with 8 waves (W8A16).  Each wave computes 64 x 64,
+//                         which lies in one (row block, column block) pair of scale blocks, so every 128-wide K
+//                         block has one scale factor per wave: s_x s_w (W8A8) or s_w (W8A16).  The wave's 64 x 64 is
 //                         2 x 2 blocks of 32 x 32 on the matrix cores (v_mfma_i32_32x32x32_i8, or
 //                         v_mfma_f32_32x32x16_bf16).  The matrix cores accumulate one K block exactly (int32) or in
 //                         fp32; at its end the partial sums are scaled and added to the fp32 accumulators (INT8: the
 //                         int32 sums start from a float's bit pattern, so that one exact subtraction replaces the
-//                         int-to-float conversion).
-//                         Operands stream through a 2-stage LDS ring of 128-byte row slices (direct-to-LDS
-//                         buffer loads, one stage ahead); the fold of one K block overlaps the next one's matrix ops.
+//                         int-to-float conversion).  Operands stream through LDS rings of 128-byte row slices
+//                         (direct-to-LDS buffer loads, one or two stages ahead); the fold of one K block overlaps the
+//                         next one's matrix ops.
 #include <algorithm>
+#include <climits>
+#include <numeric>
 #include <type_traits>
 
 #include "linear_internal.h"
@@ -108,6 +111,7 @@ __global__ void __launch_bounds__(kLinThreads) codes_to_bf16_kernel(const int8_t
 // ---------------------------------------------------------------------------------------------------------
 // The GEMM.
 constexpr int kLinRow = 128;  // bytes of one operand row per LDS stage
+constexpr int kLinLdsMax = 160 * 1024;  // LDS of a compute unit
 
 // The INT8 partial sums of a K block start from the bit pattern of the float 1/(2 pi) (an inline constant of the
 // matrix-core instruction).  A K block's sum obeys |S| <= 128 * 127^2 < 2^21, and adding S to that pattern stays in
@@ -118,24 +122,44 @@ constexpr int kLinRow = 128;  // bytes of one operand row per LDS stage
 [[maybe_unused]] constexpr int kI8Bias = 0x3E22F983;
 [[maybe_unused]] constexpr float kI8BiasF = 0.15915494309189535f;  // the float with those bits
 [[maybe_unused]] constexpr float kI8Unit = 67108864.0f;            // 2^26
-constexpr int kLinRing = 2;   // LDS ring stages
 
-template <bool A8>
+// Tile geometry.  WR rows x 2 columns of waves, each wave computing 64 x 64: WR = 4 gives a 256 x 128 tile (8 waves,
+// one workgroup per compute unit, a 3-stage ring loaded two stages ahead), WR = 2 a 128 x 128 tile (4 waves, two
+// workgroups per compute unit, a 2-stage ring loaded one stage ahead).  Both keep about 64-96 KiB of tile loads in
+// flight per compute unit; the wide tile streams a quarter fewer operand bytes per matrix op.
+//
+// A stage holds HALVES 128-row activation slices and one 128-row weight slice of ROW bytes each.  Each slice has a
+// ring of its own in LDS (R slots of 16 KiB), then come the per-K-block scale lists (one per 128-row block of the
+// tile): a wave's operands then lie in two rings whose slots sit at most 32 KiB apart, within the 16-bit immediate
+// offset of an LDS read.
+template <bool A8, int WR>
 struct LinGeo {
-  static constexpr int EB = A8 ? 1 : 2;           // bytes per operand element
-  static constexpr int ROW = kLinRow;             // bytes of one operand row per stage (granules of 16 B)
-  static constexpr int G16 = ROW / 16;            // granules per row
-  static constexpr int SPB = kLinBlk * EB / ROW;  // stages per 128-wide K block
-  static constexpr int KSTEPS = ROW / 32;         // matrix-core k-steps per stage, 32 bytes of K each
-  static constexpr int TILE = kLinBlk * ROW;      // one operand slice: 128 rows x ROW bytes
-  static constexpr int STAGE = 2 * TILE;          // activations + weights
-  static constexpr int R = kLinRing;              // ring stages
-  static constexpr int DIST = R - 1;              // a stage is loaded this many stages ahead of its use
-  static constexpr int LPT = TILE / (16 * kLinThreads);  // 16-byte loads per thread per slice
-  static constexpr int OPS = 2 * LPT;                    // loads per thread per stage
-  static constexpr int BYTES = R * STAGE;                // the per-K-block scale list follows
-  static_assert(LPT * 16 * kLinThreads == TILE, "slices split into whole loads");
-  static_assert(R % SPB == 0 || SPB % R == 0, "ring slots follow the unrolled stages");
+  static constexpr int NW = 2 * WR;                 // waves
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int TM = 64 * WR;                // activation (output) rows of a tile
+  static constexpr int HALVES = TM / kLinBlk;       // 128-row activation slices (row blocks) of a tile
+  static constexpr int EB = A8 ? 1 : 2;             // bytes per operand element
+  static constexpr int ROW = kLinRow;               // bytes of one operand row per stage (granules of 16 B)
+  static constexpr int G16 = ROW / 16;              // granules per row
+  static constexpr int SPB = kLinBlk * EB / ROW;    // stages per 128-wide K block
+  static constexpr int KSTEPS = ROW / 32;           // matrix-core k-steps per stage, 32 bytes of K each
+  static constexpr int SL = kLinBlk * ROW;          // one slice of a stage: 128 rows x ROW bytes
+  static constexpr int R = WR == 4 ? 3 : 2;         // ring stages
+  static constexpr int DIST = R - 1;                // a stage is loaded this many stages ahead of its use
+  static constexpr int RING = R * SL;               // the ring of one slice
+  static constexpr int NSL = HALVES + 1;            // slices per stage
+  static constexpr int BOFF = HALVES * RING;        // the weight ring follows the activation rings
+  static constexpr int BYTES = NSL * RING;          // the scale lists follow
+  static constexpr int LPS = SL / (16 * THREADS);   // 16-byte loads per thread per slice
+  static constexpr int OPS = NSL * LPS;             // loads per thread per stage
+  static constexpr int SETS = A8 ? 2 : 1;           // partial-sum register sets
+  // K blocks after which the pattern of (first ring slot, register set) repeats
+  static constexpr int PERIOD = std::lcm(R / std::gcd(R, SPB), SETS);
+  static constexpr int MAX_KB = (kLinLdsMax - BYTES) / (4 * HALVES);  // K blocks the scale lists have room for
+  static_assert(LPS * 16 * THREADS == SL, "slices split into whole loads");
+  static_assert((R - 1) * SL < 65536, "slot offsets fit the immediate offset of an LDS read");
+  static_assert(NW * 64 * 64 * 2 <= BYTES, "the epilogue stages the bf16 tile in the rings");
+  static_assert((DIST - 1) * OPS < 64, "the wait count fits vmcnt");
 };
 
 // XOR swizzles of the 16-byte granules of an LDS row (4 or 8 granules).  The 16 lanes of a quarter-wave read 16
@@ -176,26 +200,35 @@ __device__ __forceinline__ v16f mma_bf16(const v8bf& a, const v8bf& b, const v16
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// The K loop runs stage by stage: wait for the stage, barrier, load the next stage into the other slot, run the
-// stage's k-steps on the matrix cores.  The partial sums of consecutive K blocks alternate between two register
-// sets, so the scaled fold of K block kb - 1 into the fp32 accumulators is independent of the matrix ops of K block
-// kb and sits in the same scheduling region: the vector ALU works while the matrix cores run.
-template <bool A8>
-__global__ void __launch_bounds__(kLinThreads, 2) linear_kernel(LinearArg p) {
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// The K loop runs stage by stage: wait for the stage, barrier, load stage t + DIST into the slot stage t - 1 used, run
+// the stage's k-steps on the matrix cores.  The partial sums of consecutive K blocks alternate between two register
+// sets (INT8), so the scaled fold of K block kb - 1 into the fp32 accumulators is independent of the matrix ops of K
+// block kb and sits in the same scheduling region: the vector ALU works while the matrix cores run.  Ring slots and
+// register sets are compile-time: the loop body covers PERIOD K blocks.
+template <bool A8, int WR>
+__global__ void __launch_bounds__(128 * WR, 4 / WR) linear_kernel(LinearArg p) {
   // (the body is device code only: the host pass needs just the signature for the launch stub, and it would drop the
   // stub over the target builtins and register constraints below)
 #if defined(__HIP_DEVICE_COMPILE__)
-  using G = LinGeo<A8>;
+  using G = LinGeo<A8, WR>;
   using Part = std::conditional_t<A8, v16i, v16f>;  // one K block's partial sums of a 32 x 32 block
   using Opnd = std::conditional_t<A8, v4i, v8bf>;
-  constexpr int R = G::R;
+  constexpr int R = G::R, NW = G::NW, G16 = G::G16;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int n32 = lane & 31, g = lane >> 5;
-  const int mtiles = (p.M + kLinBlk - 1) / kLinBlk, ntiles = (p.N + kLinBlk - 1) / kLinBlk;
+  const int mtiles = (p.M + G::TM - 1) / G::TM, ntiles = (p.N + kLinBlk - 1) / kLinBlk;
   const int nkb = p.K / kLinBlk;
 
   // output tile: XCD-contiguous ranges, then groups of 4 row tiles walked column tile by column tile, so the
@@ -207,27 +240,33 @@ __global__ void __launch_bounds__(kLinThreads, 2) linear_kernel(LinearArg p) {
   const int gm = min(GM, mtiles - first);
   const int within = logical - grp * GM * ntiles;
   const int mt = first + within % gm, nt = within / gm;
-  const int m0 = mt * kLinBlk, n0 = nt * kLinBlk;
+  const int m0 = mt * G::TM, n0 = nt * kLinBlk;
 
-  // the scale factor of every K block of this tile, after the ring
+  // the scale factor of every K block, for each 128-row block of the tile (0 for a block past M: its rows are zero
+  // and never stored), after the rings; each wave uses the list of its own row block
+  const int mblocks = (p.M + kLinBlk - 1) / kLinBlk;
   float* cs = reinterpret_cast<float*>(smem + G::BYTES);
-  for (int kb = threadIdx.x; kb < nkb; kb += kLinThreads)
-    cs[kb] = A8 ? p.sx[(int64_t)mt * nkb + kb] * p.sw[(int64_t)nt * nkb + kb] : p.sw[(int64_t)nt * nkb + kb];
-  __syncthreads();  // a full workgroup barrier: the list is written with ordinary LDS stores (no tile load in flight yet)
+  for (int e = threadIdx.x; e < G::HALVES * nkb; e += G::THREADS) {
+    const int h = e / nkb, kb = e - h * nkb, rb = mt * G::HALVES + h;
+    float v = p.sw[(int64_t)nt * nkb + kb];
+    if constexpr (A8) v = (rb < mblocks) ? p.sx[(int64_t)rb * nkb + kb] * v : 0.0f;
+    cs[e] = v;
+  }
+  const int half = G::HALVES > 1 ? (64 * wm) / kLinBlk : 0;  // this wave's activation slice
+  const float* csw = cs + half * nkb;
+  __syncthreads();  // a full workgroup barrier: the lists are written with ordinary LDS stores (no tile load yet)
 
-  // the tile's rows; a stage reads them through a buffer that starts at its K offset and ends after the last row in
-  // the matrix, so rows past M (N) read as zero
-  const int arows = min(kLinBlk, p.M - m0), brows = min(kLinBlk, p.N - n0);
+  // the slices' rows: a stage reads them through a buffer that starts at its K offset and ends after the last row in
+  // the matrix, so rows past M (N) read as zero (an activation slice wholly past M has an empty buffer)
+  const int arows = min(G::TM, p.M - m0), brows = min(kLinBlk, p.N - n0);
   const uint8_t* abase = p.a + (int64_t)m0 * p.lda;
   const uint8_t* bbase = p.b + (int64_t)n0 * p.ldb;
-  const int abytes = arows * (int)p.lda, bbytes = brows * (int)p.ldb;
-  // load plan: load j of this wave fills LDS granules [(4 j + wave) * 64, +64) of a slice; LDS granule q holds row
+  // load plan: load j of this wave fills LDS granules [(NW j + wave) * 64, +64) of a slice; LDS granule q holds row
   // q / G16, logical granule (q % G16) ^ lswz(row).  The K offset of a stage goes in the buffer base.
-  constexpr int G16 = G::G16;
-  int la[G::LPT], lb[G::LPT];
+  int la[G::LPS], lb[G::LPS];
 #pragma unroll
-  for (int j = 0; j < G::LPT; ++j) {
-    const int q = (4 * j + wave) * 64 + lane;
+  for (int j = 0; j < G::LPS; ++j) {
+    const int q = (NW * j + wave) * 64 + lane;
     const int row = q / G16, lg = (q % G16) ^ lswz<G16>(row);
     la[j] = row * (int)p.lda + 16 * lg;
     lb[j] = row * (int)p.ldb + 16 * lg;
@@ -237,27 +276,36 @@ __global__ void __launch_bounds__(kLinThreads, 2) linear_kernel(LinearArg p) {
   // splits the loop body) into ring slot SLOT
   auto issue = [&](int t, auto slot_tag) __attribute__((always_inline)) {
     constexpr int SLOT = decltype(slot_tag)::value;
-    uint8_t* st = smem + SLOT * G::STAGE;
     const int kbyte = min(t, T - 1) * G::ROW;
     // (a row's bytes from kbyte on stay inside the buffer: kbyte + ROW <= K * EB <= ld)
-    const auto ra = rows_rsrc(abase + kbyte, abytes - kbyte);
-    const auto rb = rows_rsrc(bbase + kbyte, bbytes - kbyte);
+    const auto rb = rows_rsrc(bbase + kbyte, brows * (int)p.ldb - kbyte);
 #pragma unroll
-    for (int j = 0; j < G::LPT; ++j) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(st + (4 * j + wave) * 1024), 16, la[j], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(st + G::TILE + (4 * j + wave) * 1024), 16, lb[j], 0,
-                                               0, 0);
+    for (int h = 0; h < G::HALVES; ++h) {
+      const int hrows = min(kLinBlk, arows - kLinBlk * h);
+      const auto ra = rows_rsrc(abase + (int64_t)kLinBlk * h * p.lda + kbyte, max(hrows * (int)p.lda - kbyte, 0));
+      uint8_t* sa = smem + h * G::RING + SLOT * G::SL;
+#pragma unroll
+      for (int j = 0; j < G::LPS; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(sa + (NW * j + wave) * 1024), 16, la[j], 0, 0, 0);
     }
+    uint8_t* sb = smem + G::BOFF + SLOT * G::SL;
+#pragma unroll
+    for (int j = 0; j < G::LPS; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(sb + (NW * j + wave) * 1024), 16, lb[j], 0, 0, 0);
   };
-  // operand reads: 32-row block i of this wave, k-step s: row (64 w + 32 i + lane % 32), logical granule 2 s + lane / 32
+  // operand reads: 32-row block i of this wave, k-step s: row (64 w + 32 i + lane % 32) of its slice, logical granule
+  // 2 s + lane / 32.  Where ring and slot offsets together would pass the 16-bit immediate offset of an LDS read (the
+  // wide tile), the addresses carry the offset of their ring, kept opaque to the compiler, and the immediate is only
+  // the slot's.
   int ard[2][G::KSTEPS], brd[2][G::KSTEPS];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int arow = 64 * wm + 32 * i + n32, brow = 64 * wn + 32 * i + n32;
+    const int arow = 64 * wm + 32 * i + n32 - kLinBlk * half, brow = 64 * wn + 32 * i + n32;
 #pragma unroll
     for (int s = 0; s < G::KSTEPS; ++s) {
-      ard[i][s] = arow * G::ROW + 16 * ((2 * s + g) ^ lswz<G16>(arow));
-      brd[i][s] = G::TILE + brow * G::ROW + 16 * ((2 * s + g) ^ lswz<G16>(brow));
+      ard[i][s] = half * G::RING + arow * G::ROW + 16 * ((2 * s + g) ^ lswz<G16>(arow));
+      brd[i][s] = G::BOFF + brow * G::ROW + 16 * ((2 * s + g) ^ lswz<G16>(brow));
+      if constexpr (G::BOFF + (R - 1) * G::SL + G::SL > 65536) asm("" : "+v"(ard[i][s]), "+v"(brd[i][s]));
     }
   }
 
@@ -272,11 +320,13 @@ __global__ void __launch_bounds__(kLinThreads, 2) linear_kernel(LinearArg p) {
 
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
+  using I0 = std::integral_constant<int, 0>;
+  using I2 = std::integral_constant<int, 2>;
   // fold rows-block range [I0, I1) of register set SET (scale factor fc) into the accumulators
   auto fold = [&](float fc, auto set_tag, auto i0_tag, auto i1_tag) __attribute__((always_inline)) {
-    constexpr int SET = decltype(set_tag)::value, I0 = decltype(i0_tag)::value, I1 = decltype(i1_tag)::value;
+    constexpr int SET = decltype(set_tag)::value, FI0 = decltype(i0_tag)::value, FI1 = decltype(i1_tag)::value;
 #pragma unroll
-    for (int i = I0; i < I1; ++i)
+    for (int i = FI0; i < FI1; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -288,8 +338,8 @@ __global__ void __launch_bounds__(kLinThreads, 2) linear_kernel(LinearArg p) {
         }
   };
   // stage t (ring slot SLOT) into register set SET: wait until the stage has landed for every wave, refill the slot
-  // of stage t - 1 with stage t + DIST, run the k-steps (FRESH: the first stage of a K block, from zero), and fold
-  // the part [FI0, FI1) of the other register set (the previous K block, scale factor fc)
+  // of stage t - 1 with stage t + DIST, run the k-steps (FRESH: the first stage of a K block, from its start value),
+  // and fold the part [FI0, FI1) of the other register set (the previous K block, scale factor fc)
   auto stage = [&](int t, auto slot_tag, auto set_tag, auto fresh_tag, auto fi0_tag, auto fi1_tag, float fc)
       __attribute__((always_inline)) {
     constexpr int SLOT = decltype(slot_tag)::value, SET = decltype(set_tag)::value;
@@ -297,7 +347,7 @@ __global__ void __launch_bounds__(kLinThreads, 2) linear_kernel(LinearArg p) {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((G::DIST - 1) * G::OPS) : "memory");  // this wave's loads of stage t
     ring_sync();  // ... and every other wave's; all reads of stage t - 1 are done, so its slot can be refilled
     issue(t + G::DIST, std::integral_constant<int, (SLOT + G::DIST) % R>{});
-    const uint8_t* st = smem + SLOT * G::STAGE;
+    const uint8_t* st = smem + SLOT * G::SL;  // (the read addresses include the offset of their ring)
 #pragma unroll
     for (int s = 0; s < G::KSTEPS; ++s) {
       Opnd av[2], bv[2];
@@ -324,66 +374,82 @@ __global__ void __launch_bounds__(kLinThreads, 2) linear_kernel(LinearArg p) {
     }
     fold(fc, std::integral_constant<int, SET ^ 1>{}, fi0_tag, fi1_tag);
   };
-  // one K block whose first stage sits in ring slot SLOT0, into register set SET; with FOLD, the previous K block
-  // (other set) is folded in halves over the first two stages (INT8) or all at once in the first (one stage)
-  auto kblock = [&](int kb, auto slot0_tag, auto set_tag, auto fold_tag) __attribute__((always_inline)) {
-    constexpr int SLOT0 = decltype(slot0_tag)::value;
+  // K block kb, at position PH of the period (kb = PH mod PERIOD): its first stage sits in ring slot PH SPB mod R and
+  // its partial sums go to register set PH mod 2 (INT8; set 1 for bf16).  With FOLD, the previous K block (the other
+  // set) is folded in halves over its first two stages, or all at once in its only stage.
+  auto kblock = [&](int kb, auto ph_tag, auto fold_tag) __attribute__((always_inline)) {
+    constexpr int PH = decltype(ph_tag)::value;
+    constexpr int SLOT0 = (PH * G::SPB) % R, SET = A8 ? PH % 2 : 1;
     constexpr bool FOLD = decltype(fold_tag)::value;
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, FOLD ? (G::SPB >= 2 ? 1 : 2) : 0>;
-    using I2 = std::integral_constant<int, FOLD ? 2 : 0>;
-    const float fc = FOLD ? cs[kb - 1] : 0.0f;
-    stage(kb * G::SPB, slot0_tag, set_tag, std::true_type{}, I0{}, I1{}, fc);
-#pragma unroll
-    for (int u = 1; u < G::SPB; ++u) {
-      // (u is a compile-time constant after unrolling; the slot and the fold range follow from it)
-      if (u == 1)
-        stage(kb * G::SPB + 1, std::integral_constant<int, (SLOT0 + 1) % R>{}, set_tag, std::false_type{}, I1{},
-              I2{}, fc);
-      else if (u == 2)
-        stage(kb * G::SPB + 2, std::integral_constant<int, (SLOT0 + 2) % R>{}, set_tag, std::false_type{}, I0{},
-              I0{}, 0.0f);
-      else
-        stage(kb * G::SPB + 3, std::integral_constant<int, (SLOT0 + 3) % R>{}, set_tag, std::false_type{}, I0{},
-              I0{}, 0.0f);
-    }
+    using FI1 = std::integral_constant<int, FOLD ? (G::SPB >= 2 ? 1 : 2) : 0>;
+    using FI2 = std::integral_constant<int, FOLD ? 2 : 0>;
+    using SetT = std::integral_constant<int, SET>;
+    const float fc = FOLD ? csw[kb - 1] : 0.0f;
+    stage(kb * G::SPB, std::integral_constant<int, SLOT0>{}, SetT{}, std::true_type{}, I0{}, FI1{}, fc);
+    static_for<1, G::SPB>([&](auto u_tag) __attribute__((always_inline)) {
+      constexpr int U = decltype(u_tag)::value;
+      using Lo = std::integral_constant<int, U == 1 ? FI1::value : 0>;
+      using Hi = std::integral_constant<int, U == 1 ? FI2::value : 0>;
+      stage(kb * G::SPB + U, std::integral_constant<int, (SLOT0 + U) % R>{}, SetT{}, std::false_type{}, Lo{}, Hi{},
+            U == 1 ? fc : 0.0f);
+    });
   };
-  using I0 = std::integral_constant<int, 0>;
-  using I2 = std::integral_constant<int, 2>;
-  // prologue: stages 0 .. DIST-1 (clamped) into slots 0 .. DIST-1
+  // prologue: stages 0 .. DIST-1 into slots 0 .. DIST-1
   issue(0, S0{});
   if constexpr (G::DIST > 1) issue(1, S1{});
-  if constexpr (G::DIST > 2) issue(2, std::integral_constant<int, 2>{});
-  static_assert(G::DIST <= 3, "the prologue issues DIST stages");
-  constexpr int KSLOTS = (G::SPB * 2) % R;  // slot advance over two K blocks
-  static_assert(KSLOTS == 0, "two K blocks fill the ring a whole number of times");
+  static_assert(G::DIST <= 2, "the prologue issues DIST stages");
+  constexpr int P = G::PERIOD;
   if constexpr (A8) {
     // INT8: the fold costs as much vector work as a K block's matrix ops; two register sets overlap them
-    kblock(0, S0{}, S0{}, std::false_type{});
+    kblock(0, I0{}, std::false_type{});
     int kb = 1;
-    constexpr int SLOT_ODD = G::SPB % R;  // first slot of an odd K block
-    for (; kb + 1 < nkb; kb += 2) {
-      kblock(kb, std::integral_constant<int, SLOT_ODD>{}, S1{}, std::true_type{});
-      kblock(kb + 1, S0{}, S0{}, std::true_type{});
-    }
-    if (kb < nkb) {  // nkb even: the last K block (odd) goes to set 1
-      kblock(kb, std::integral_constant<int, SLOT_ODD>{}, S1{}, std::true_type{});
-      fold(cs[nkb - 1], S1{}, I0{}, I2{});
+    if constexpr (P == 2) {
+      // (the plain two-block form: the compiler interleaves the fold with the matrix ops of both blocks)
+      for (; kb + 1 < nkb; kb += 2) {
+        kblock(kb, S1{}, std::true_type{});
+        kblock(kb + 1, S0{}, std::true_type{});
+      }
+      if (kb < nkb) {
+        kblock(kb, S1{}, std::true_type{});
+        fold(csw[nkb - 1], S1{}, I0{}, I2{});
+      } else {
+        fold(csw[nkb - 1], S0{}, I0{}, I2{});
+      }
     } else {
-      fold(cs[nkb - 1], S0{}, I0{}, I2{});
+      for (; kb + P <= nkb; kb += P)
+        static_for<1, P + 1>([&](auto u_tag) __attribute__((always_inline)) {
+          constexpr int U = decltype(u_tag)::value;
+          kblock(kb + U - 1, std::integral_constant<int, U % P>{}, std::true_type{});
+        });
+      const int rest = nkb - kb;  // 0 .. P - 1 more K blocks, at positions 1 .. rest
+      static_for<1, P>([&](auto u_tag) __attribute__((always_inline)) {
+        constexpr int U = decltype(u_tag)::value;
+        if (U <= rest) kblock(kb + U - 1, std::integral_constant<int, U>{}, std::true_type{});
+      });
+      if ((nkb - 1) & 1) fold(csw[nkb - 1], S1{}, I0{}, I2{});
+      else fold(csw[nkb - 1], S0{}, I0{}, I2{});
     }
   } else {
-    // bf16: four times the matrix work per fold and one register set (two would not fit with the wider operands);
-    // every K block fills the ring exactly, so each starts in slot 0
-    static_assert(G::SPB % R == 0, "a bf16 K block starts in slot 0");
-    for (int kb = 0; kb < nkb; ++kb) {
-      kblock(kb, S0{}, S1{}, std::false_type{});
-      fold(cs[kb], S1{}, I0{}, I2{});
-    }
+    // bf16: four times the matrix work per fold and one register set (two would not fit with the wider operands)
+    int kb = 0;
+    for (; kb + P <= nkb; kb += P)
+      static_for<0, P>([&](auto u_tag) __attribute__((always_inline)) {
+        constexpr int U = decltype(u_tag)::value;
+        kblock(kb + U, std::integral_constant<int, U>{}, std::false_type{});
+        fold(csw[kb + U], S1{}, I0{}, I2{});
+      });
+    const int rest = nkb - kb;
+    static_for<0, P - 1>([&](auto u_tag) __attribute__((always_inline)) {
+      constexpr int U = decltype(u_tag)::value;
+      if (U < rest) {
+        kblock(kb + U, std::integral_constant<int, U>{}, std::false_type{});
+        fold(csw[kb + U], S1{}, I0{}, I2{});
+      }
+    });
   }
 
-  // epilogue through LDS (the ring is free once every wave is past its last stage and the extra load of the last
-  // stage has landed): the wave writes its 64 x 64 block as bf16 rows of 128 bytes, then stores them 16 bytes per
+  // epilogue through LDS (the rings are free once every wave is past its last stage and the extra loads of the last
+  // stage have landed): the wave writes its 64 x 64 block as bf16 rows of 128 bytes, then stores them 16 bytes per
   // lane.  Lane holds column 32 j + lane % 32 of the block; register r of block i is row
   // 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -423,19 +489,19 @@ __global__ void __launch_bounds__(kLinThreads, 2) linear_kernel(LinearArg p) {
 #endif
 }
 
-template <bool A8>
+template <bool A8, int WR>
 hipError_t launch_linear_t(const LinearArg& p, hipStream_t s) {
-  using G = LinGeo<A8>;
-  const int mtiles = (p.M + kLinBlk - 1) / kLinBlk, ntiles = (p.N + kLinBlk - 1) / kLinBlk;
-  const size_t bytes = G::BYTES + (size_t)(p.K / kLinBlk) * sizeof(float);
-  static bool configured[2] = {false, false};
-  if (!configured[A8]) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_kernel<A8>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+  using G = LinGeo<A8, WR>;
+  const int mtiles = (p.M + G::TM - 1) / G::TM, ntiles = (p.N + kLinBlk - 1) / kLinBlk;
+  const size_t bytes = G::BYTES + (size_t)G::HALVES * (p.K / kLinBlk) * sizeof(float);
+  static bool configured = false;
+  if (!configured) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_kernel<A8, WR>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, kLinLdsMax);
     if (e != hipSuccess) return e;
-    configured[A8] = true;
+    configured = true;
   }
-  linear_kernel<A8><<<(unsigned)(mtiles * ntiles), kLinThreads, bytes, s>>>(p);
+  linear_kernel<A8, WR><<<(unsigned)(mtiles * ntiles), G::THREADS, bytes, s>>>(p);
   return hipGetLastError();
 }
 
@@ -456,7 +522,14 @@ hipError_t launch_codes_to_bf16(const int8_t* codes, uint16_t* out, int64_t n, h
 }
 
 hipError_t launch_linear(bool w8a8, const LinearArg& p, hipStream_t s) {
-  return w8a8 ? launch_linear_t<true>(p, s) : launch_linear_t<false>(p, s);
+  // INT8 keeps the 128-row tile: its fold hides best under the matrix ops of the other workgroup's wave on the same
+  // SIMD, and the 8-wave tile (two waves of one workgroup per SIMD, in step) measured no faster.  bf16 takes the
+  // 256-row tile once there is more than one row block, its scale lists fit beside the rings, and 256 activation rows
+  // span less than 2^31 bytes (the buffer offsets and extents are 32-bit).
+  if (w8a8) return launch_linear_t<true, 2>(p, s);
+  if (p.M > kLinBlk && p.lda * 256 <= INT32_MAX && p.K / kLinBlk <= LinGeo<false, 4>::MAX_KB)
+    return launch_linear_t<false, 4>(p, s);
+  return launch_linear_t<false, 2>(p, s);
 }
 
 }  // namespace sattn

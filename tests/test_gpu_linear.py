@@ -106,6 +106,17 @@ def test_linear_small(name, M, N, K, with_bias):
     close_to_exact(val(bits(y16)), ref16, exact, f"{name} W8A16")
 
 
+def test_linear_w8a16_long_k():
+    """W8A16 with more K blocks than the 256-row tile keeps scale lists for (2049): the 128-row tile takes over at
+    M > 128 (three row tiles, the last one ragged)."""
+    M, N, K = 300, 16, 2049 * BLK
+    x, w, b = wl.linear_host_inputs(M, N, K, seed=74)
+    wq, sw = sattn.quantize_blocks(w.cuda())
+    y = sattn.linear(x.cuda(), wq, sw, b.cuda(), mode=sattn.SATTN_LINEAR_W8A16)
+    ref, mag = oracle.linear_w8a16(bits(x), wq.cpu().numpy(), sw.cpu().numpy(), bits(b))
+    check(bits(y), ref, mag, K, False, "long-K W8A16")
+
+
 def test_linear_strided_and_batched():
     """x with a row stride wider than K and leading batch dimensions; y written into a wider output buffer."""
     M, N, K = 2 * 96, 256, 256
