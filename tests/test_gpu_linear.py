@@ -117,6 +117,21 @@ def test_linear_w8a16_long_k():
     check(bits(y), ref, mag, K, False, "long-K W8A16")
 
 
+def test_linear_w8a16_wide_row_stride():
+    """W8A16 reads bf16 x at the caller's row stride: at 2^22 + 8 elements, 256 rows span more than 2^31 bytes, so
+    the 128-row tile takes over at M > 128 (x occupies about 1.1 GB on the device; only K columns are read)."""
+    M, N, K = 129, 24, 128
+    ldx = (1 << 22) + 8
+    x, w, b = wl.linear_host_inputs(M, N, K, seed=75)
+    xd = torch.zeros((M, ldx), dtype=torch.bfloat16, device="cuda")
+    xd[:, :K] = x.cuda()
+    wq, sw = sattn.quantize_blocks(w.cuda())
+    y = sattn.linear(xd[:, :K], wq, sw, b.cuda(), mode=sattn.SATTN_LINEAR_W8A16)
+    ref, mag = oracle.linear_w8a16(bits(x), wq.cpu().numpy(), sw.cpu().numpy(), bits(b))
+    check(bits(y), ref, mag, K, False, "wide-stride W8A16")
+    del xd
+
+
 def test_linear_strided_and_batched():
     """x with a row stride wider than K and leading batch dimensions; y written into a wider output buffer."""
     M, N, K = 2 * 96, 256, 256
