@@ -82,6 +82,7 @@ LARGE = [
     ("wan14b-480p", W["wan14b-480p"], 2),
     ("wan14b-720p", W["wan14b-720p"], 2),
     ("wan14b-720p", W["wan14b-720p"], 1),
+    ("wan14b-720p", W["wan14b-720p"], 0),
     ("layersel-720p-cross", W["layersel-720p-cross"], 0),
     ("layersel-720p-cross", W["layersel-720p-cross"], 2),
 ]
