@@ -132,6 +132,27 @@ def test_deterministic_and_no_out_of_bounds_writes():
         assert torch.all(big[w.B * w.H * w.Nq * w.d:] == 0x7ABC), f"mode {mode} wrote past O"
 
 
+def test_calls_follow_the_current_stream():
+    """The entry points enqueue on the caller's current stream: quantize + attention and the linear layer called under
+    a side stream (default priority) give the same bits as on the default stream once that stream alone is waited for."""
+    w = wl.scaled(W["wan14b-720p"], name="stream", H=2, Nq=300, Nkv=260, seed=41)
+    q, k, v = device_inputs(w)
+    x = torch.randn((300, 256), device="cuda").to(torch.bfloat16)
+    wt = (torch.randn((136, 256), device="cuda") * 0.06).to(torch.bfloat16)
+    ref_o = sattn.fwd(q, k, v, mode=2, sm_scale=w.sm_scale)
+    wq, sw = sattn.quantize_blocks(wt)
+    ref_y = sattn.linear(x, wq, sw, mode=sattn.SATTN_LINEAR_W8A8)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        o = sattn.fwd(q, k, v, mode=2, sm_scale=w.sm_scale)
+        y = sattn.linear(x, wq, sw, mode=sattn.SATTN_LINEAR_W8A8)
+    side.synchronize()
+    assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16))
+    assert torch.equal(y.view(torch.int16), ref_y.view(torch.int16))
+
+
 def test_strided_layout_matches_dense():
     w = wl.scaled(W["wan14b-720p"], name="nhd", H=4, Nq=300, Nkv=260, seed=21)
     for mode in (0, 1, 2):
