@@ -91,6 +91,30 @@ __global__ void __launch_bounds__(256) quant_q_kernel(TensorArg q, QuantArg qa) 
 }
 
 // ---------------------------------------------------------------------------------------------- K/V stats
+// Rows t0 .. t1-1 of 8 bf16 channels folded into acc in row order: fp32 sum, or (MAXABS) max |x|.  The loads of
+// kStatBatch rows are issued together, then folded one after another, so the order of the additions is the plain
+// sequential one while a thread has many loads in flight (a run is all the parallelism one thread has, and a
+// short sequence gives few runs).
+constexpr int kStatBatch = 16;
+template <bool MAXABS>
+__device__ __forceinline__ void run_reduce(const uint16_t* p, int64_t sn, int t0, int t1, float (&acc)[8]) {
+  auto fold = [&](const uint4& u) {
+    float f[8];
+    unpack8(u, f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = MAXABS ? fmaxf(acc[i], fabsf(f[i])) : acc[i] + f[i];
+  };
+  int t = t0;
+  for (; t + kStatBatch <= t1; t += kStatBatch) {
+    uint4 u[kStatBatch];
+#pragma unroll
+    for (int j = 0; j < kStatBatch; ++j) u[j] = *reinterpret_cast<const uint4*>(p + (int64_t)(t + j) * sn);
+#pragma unroll
+    for (int j = 0; j < kStatBatch; ++j) fold(u[j]);
+  }
+  for (; t < t1; ++t) fold(*reinterpret_cast<const uint4*>(p + (int64_t)t * sn));
+}
+
 // Per 64-token run and channel: sequential fp32 sum of K, and max |V| (mode 2).  Thread owns 8 channels of
 // one run; grid (ceil(nkb / RUNS), H, B) with RUNS runs per 256-thread block.
 template <int D>
@@ -106,24 +130,14 @@ __global__ void __launch_bounds__(256) kv_stats_kernel(TensorArg k, TensorArg v,
   const int t1 = min(t0 + kChunk, qa.Nkv);
   const uint16_t* ks = k.ptr + b * k.sb + h * k.sh + c0;
   float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int t = t0; t < t1; ++t) {
-    float f[8];
-    unpack8(*reinterpret_cast<const uint4*>(ks + (int64_t)t * k.sn), f);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s[i] = s[i] + f[i];
-  }
+  run_reduce<false>(ks, k.sn, t0, t1, s);
   const int64_t o = (((int64_t)b * qa.H + h) * qa.nkb + run) * D + c0;
   *reinterpret_cast<float4*>(ksum + o) = make_float4(s[0], s[1], s[2], s[3]);
   *reinterpret_cast<float4*>(ksum + o + 4) = make_float4(s[4], s[5], s[6], s[7]);
   if (with_v) {
     const uint16_t* vs = v.ptr + b * v.sb + h * v.sh + c0;
     float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int t = t0; t < t1; ++t) {
-      float f[8];
-      unpack8(*reinterpret_cast<const uint4*>(vs + (int64_t)t * v.sn), f);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf(f[i]));
-    }
+    run_reduce<true>(vs, v.sn, t0, t1, m);
     *reinterpret_cast<float4*>(vmax + o) = make_float4(m[0], m[1], m[2], m[3]);
     *reinterpret_cast<float4*>(vmax + o + 4) = make_float4(m[4], m[5], m[6], m[7]);
   }
