@@ -430,7 +430,8 @@ def main():
     achieved = w.ops / (attn_ms * 1e-3) / 1e12
     traffic_detail = measured_traffic(w.name, mode, w.ops)
     line = {
-        "metric": METRIC,
+        # the headline workload keeps the headline metric's name; the others name their own workload
+        "metric": METRIC if w.name == "wan14b-720p" else f"effective attention TOPS + % INT8 MFMA peak, {w.name}",
         "value": round(value, 2),
         "unit": "TOPS",
         "n_gpus": 1,
