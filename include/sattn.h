@@ -42,6 +42,8 @@
  *     been enqueued.  No C++ exception crosses this interface.
  *   - NaN or Inf inputs are outside the contract.  Zero blocks and zero channels are inside it and give
  *     finite outputs.
+ *   - Empty shapes (B, H, N, rows or columns below 1) are SATTN_ERR_INVALID_ARG, not a silent no-op: a
+ *     softmax over no keys has no value, and a call with no queries is refused the same way.
  */
 #ifndef SATTN_H
 #define SATTN_H

@@ -112,6 +112,22 @@ def test_argument_errors_are_caught_on_the_host(S):
     assert fwd(o=_t(S, P, 1, 2, 255, 64)) == S.SATTN_ERR_INVALID_ARG       # O rows != Q rows
     assert fwd(v=_t(S, P, 1, 2, 200, 64)) == S.SATTN_ERR_INVALID_ARG       # V rows != K rows
     assert fwd(q=_t(S, P, 1, 2, 256, 64, sn=68)) == S.SATTN_ERR_INVALID_ARG  # row stride not a multiple of 8
+    # empty shapes are refused, never launched: no queries, no keys, no heads, no batch
+    assert fwd(q=_t(S, P, 1, 2, 0, 64), o=_t(S, P, 1, 2, 0, 64)) == S.SATTN_ERR_INVALID_ARG
+    assert fwd(k=_t(S, P, 1, 2, 0, 64), v=_t(S, P, 1, 2, 0, 64)) == S.SATTN_ERR_INVALID_ARG
+    assert fwd(*[_t(S, P, 1, 0, 256, 64) for _ in range(4)]) == S.SATTN_ERR_INVALID_ARG
+    assert fwd(*[_t(S, P, 0, 2, 256, 64) for _ in range(4)]) == S.SATTN_ERR_INVALID_ARG
+    assert L.sattn_cross_fwd(byref(q), byref(_t(S, P, 1, 2, 0, 64)), byref(_t(S, P, 1, 2, 0, 64)), byref(o), 0.0,
+                             0, ctypes.c_void_p(P), ws_need, None) == S.SATTN_ERR_INVALID_ARG
+    for empty in ((0, 2, 256, 256), (1, 0, 256, 256), (1, 2, 0, 256), (1, 2, 256, 0)):
+        assert S.sattn_workspace_bytes(*empty, 64, 64, 64, 2) == 0
+        assert S.sattn_quant_bytes(*empty, 64, 64, 64, 2) == 0
+    # the linear layer likewise: no tokens or no output features
+    fake = ctypes.c_void_p(P)
+    for M, N in ((0, 128), (128, 0)):
+        assert S.sattn_linear_workspace_bytes(M, N, 128, 0) == 0
+        assert L.sattn_linear_quantized(fake, fake, fake, fake, None, fake, 128, M, N, 128, None) \
+            == S.SATTN_ERR_INVALID_ARG
     bad_d = [_t(S, P, 1, 2, 256, 96) for _ in range(4)]
     assert fwd(*bad_d) == S.SATTN_ERR_UNSUPPORTED
     # mode 0 addresses K rows with 32-bit offsets: a K row stride of 2^24 elements is refused, 2^24 - 8 is not
