@@ -34,12 +34,17 @@
  *     argument are HOST memory, read only during the call.
  *   - Nothing is allocated and nothing is synchronised.  All work is enqueued on `stream` (0 = the null
  *     stream) and the call returns.  Faults inside kernels surface at the caller's next synchronisation.
- *   - The caller owns every buffer.  The library keeps no state between calls, so it is re-entrant;
- *     concurrent calls need distinct workspaces and outputs.  Outputs must not alias inputs.
+ *   - The caller owns every buffer.  The library keeps no state between calls (no flags, caches or handles;
+ *     per-kernel launch attributes are set on the current device by every call), so it is re-entrant and
+ *     serves every GPU of a process alike; concurrent calls need distinct workspaces and outputs.  Outputs
+ *     must not alias inputs.
  *   - Errors: arguments are checked on the host before any launch.  A bad argument returns
- *     SATTN_ERR_INVALID_ARG, a valid but unsupported shape SATTN_ERR_UNSUPPORTED, a too small
- *     workspace SATTN_ERR_WORKSPACE, a failed launch SATTN_ERR_HIP; in every error case nothing has
- *     been enqueued.  No C++ exception crosses this interface.
+ *     SATTN_ERR_INVALID_ARG, a valid but unsupported shape SATTN_ERR_UNSUPPORTED, a too small workspace
+ *     SATTN_ERR_WORKSPACE; in these cases nothing has been enqueued.  SATTN_ERR_HIP reports a failure of
+ *     the HIP runtime: when the per-call set-up fails, nothing has been enqueued; when a launch fails, the
+ *     kernels this call enqueued before it (which write only the workspace and the call's outputs) may
+ *     still run, and the outputs are undefined.  An error left pending by earlier, unrelated HIP calls of
+ *     the calling thread is cleared on entry and not reported.  No C++ exception crosses this interface.
  *   - NaN or Inf inputs are outside the contract.  Zero blocks and zero channels are inside it and give
  *     finite outputs.
  *   - Empty shapes (B, H, N, rows or columns below 1) are SATTN_ERR_INVALID_ARG, not a silent no-op: a

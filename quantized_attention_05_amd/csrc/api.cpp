@@ -1,6 +1,6 @@
 // C ABI of libsattn: argument checks, workspace carving, mode dispatch.  Allocates nothing, synchronises
-// nothing; every kernel is enqueued on the caller's stream.  The operations are declared and cited in
-// include/sattn.h.
+// nothing, keeps no state; every kernel is enqueued on the caller's stream.  The operations are declared and cited
+// in include/sattn.h.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -28,10 +28,16 @@ sattn_status check_shape(int B, int H, int Nq, int Nkv, int d, int blk_q, int bl
   if (d != 64 && d != 128) return SATTN_ERR_UNSUPPORTED;
   if (blk_q != 64 && blk_q != 128) return SATTN_ERR_UNSUPPORTED;
   if (blk_k != kTile) return SATTN_ERR_UNSUPPORTED;
-  // keep every element offset of the padded code arrays inside int64 and every grid dimension in range
+  // keep every element offset of the padded code arrays inside int64 and every grid dimension in range (the
+  // attention grid has one workgroup per query tile and head)
   if ((int64_t)B * H > 65535 || Nq > (1 << 28) || Nkv > (1 << 28)) return SATTN_ERR_UNSUPPORTED;
+  if ((int64_t)cdiv(Nq, attn_rows_per_workgroup()) * B * H > INT32_MAX) return SATTN_ERR_UNSUPPORTED;
   return SATTN_OK;
 }
+
+// An error left pending by earlier, unrelated HIP calls of this thread would otherwise be read back by this call's
+// launch check and reported as its own: take it off before the first launch.
+void clear_pending_error() { (void)hipGetLastError(); }
 
 struct Sizes {
   int nqb, nkb;
@@ -192,6 +198,8 @@ sattn_status fwd_common(const sattn_tensor* q, const sattn_tensor* k, const satt
   sattn_quant qk;
   layout(B, H, Nq, Nkv, d, blk_q, blk_k, mode, ws, &qk);
   void* scratch = static_cast<char*>(ws) + z.total;
+  clear_pending_error();
+  if ((st = hip_status(prepare_attn(mode, d, mask != nullptr))) != SATTN_OK) return st;
   st = do_quantize(q, k, v, mode, &qk, scratch, need - z.total, s);
   if (st != SATTN_OK) return st;
   const float c = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt((float)d);
@@ -255,6 +263,7 @@ sattn_status sattn_quantize(const sattn_tensor* q, const sattn_tensor* k, const 
   if ((st = check_tensor(v, B, H, out->Nkv, d)) != SATTN_OK) return st;
   const size_t need = scratch_bytes(B, H, out->Nkv, d, mode);
   if (need > 0 && (!scratch || scratch_bytes_ < need)) return SATTN_ERR_WORKSPACE;
+  clear_pending_error();
   return do_quantize(q, k, v, mode, out, scratch, scratch_bytes_, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -274,6 +283,8 @@ sattn_status sattn_fwd_quantized(const sattn_tensor* q, const sattn_tensor* k, c
   const TensorArg none{nullptr, 0, 0, 0};
   const TensorArg qt = mode == SATTN_MODE_BF16 ? tensor_arg(q) : none;
   const TensorArg kt = mode == SATTN_MODE_BF16 ? tensor_arg(k) : none;
+  clear_pending_error();
+  if ((st = hip_status(prepare_attn(mode, qk->d, false))) != SATTN_OK) return st;
   return hip_status(launch_attn(mode, qt, kt, quant_arg(*qk), const_cast<uint16_t*>(ot.ptr), ot.sb, ot.sh, ot.sn, c,
                                 nullptr, reinterpret_cast<hipStream_t>(stream)));
 }
@@ -308,6 +319,7 @@ sattn_status sattn_error_stats(const sattn_tensor* a, const sattn_tensor* ref, d
   if ((st = check_tensor(ref, a->B, a->H, a->N, a->d)) != SATTN_OK) return st;
   if (reinterpret_cast<uintptr_t>(out) % 8 != 0) return SATTN_ERR_INVALID_ARG;
   if ((a->d != 64 && a->d != 128) || (int64_t)a->B * a->H > 65535) return SATTN_ERR_UNSUPPORTED;
+  clear_pending_error();
   return hip_status(launch_error_stats(tensor_arg(a), tensor_arg(ref), a->B, a->H, a->N, a->d, out,
                                        reinterpret_cast<hipStream_t>(stream)));
 }
@@ -322,6 +334,7 @@ sattn_status sattn_debug_qk_int32(const sattn_quant* qk, int b, int h, int q0, i
     return SATTN_ERR_INVALID_ARG;
   const int nq_pad = cdiv(qk->Nq, qk->blk_q) * qk->blk_q, nk_pad = cdiv(qk->Nkv, kTile) * kTile;
   if ((int64_t)q0 + nq > nq_pad || (int64_t)k0 + nk > nk_pad) return SATTN_ERR_INVALID_ARG;
+  clear_pending_error();
   return hip_status(launch_debug_qk(quant_arg(*qk), b, h, q0, nq, k0, nk, out, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -332,6 +345,7 @@ sattn_status sattn_quantize_blocks(const void* x, int rows, int cols, int64_t ld
   if (cols % kLinBlk != 0 || rows > (1 << 28) || cols > (1 << 28)) return SATTN_ERR_UNSUPPORTED;
   if (ld < cols || ld % 8 != 0 || !aligned16(x) || !aligned16(codes) || reinterpret_cast<uintptr_t>(scales) % 4)
     return SATTN_ERR_INVALID_ARG;
+  clear_pending_error();
   return hip_status(launch_quant_blocks(static_cast<const uint16_t*>(x), rows, cols, ld, codes, scales,
                                         reinterpret_cast<hipStream_t>(stream)));
 }
@@ -371,6 +385,8 @@ sattn_status sattn_linear_quantized(const int8_t* xq, const float* sx, const int
   if (!aligned16(xq) || !aligned16(wq) || !aligned4(sx) || !aligned4(sw)) return SATTN_ERR_INVALID_ARG;
   LinearArg p{reinterpret_cast<const uint8_t*>(xq), K, reinterpret_cast<const uint8_t*>(wq), K, sx, sw,
               static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), ldy, M, N, K};
+  clear_pending_error();
+  if ((st = hip_status(prepare_linear(true))) != SATTN_OK) return st;
   return hip_status(launch_linear(true, p, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -387,6 +403,8 @@ sattn_status sattn_linear(const void* x, int64_t ldx, const int8_t* wq, const fl
   if (reinterpret_cast<uintptr_t>(ws) % kAlign) return SATTN_ERR_INVALID_ARG;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   uint8_t* base = static_cast<uint8_t*>(ws);
+  clear_pending_error();
+  if ((st = hip_status(prepare_linear(mode == SATTN_LINEAR_W8A8))) != SATTN_OK) return st;
   hipError_t e;
   if (mode == SATTN_LINEAR_W8A8) {
     int8_t* xq = reinterpret_cast<int8_t*>(base);

@@ -623,18 +623,22 @@ hipError_t launch_attn_t(AttnArg a, hipStream_t s) {
   const auto kernel = sparse ? &attn_pipe_kernel<MODE, D, W, true> : &attn_pipe_kernel<MODE, D, W, false>;
   // dense: the ring; block-sparse: the ring + the tile list (sized for this call's key tiles)
   const int bytes = sparse ? RG::LIST_OFF + 16 + cdiv(2 * a.qa.nkb, 16) * 16 : RG::BYTES;
-  static bool configured[2] = {false, false};
-  if (!configured[sparse]) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       sparse ? RG::SPARSE_BYTES : RG::BYTES);
-    if (e != hipSuccess) return e;
-    configured[sparse] = true;
-  }
   a.nqt = cdiv(a.qa.Nq, W * kRowsPerWave);
-  const int64_t nwg = (int64_t)a.nqt * a.qa.H * a.qa.B;
-  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const int64_t nwg = (int64_t)a.nqt * a.qa.H * a.qa.B;  // below 2^31 by the host's shape checks
   kernel<<<(int)nwg, 64 * W, bytes, s>>>(a);
   return hipGetLastError();
+}
+
+// The dynamic LDS limit of the kernel a call will launch (more than the default 64 KiB in mode 2), set on the current
+// device before anything is enqueued.  Set on every call rather than remembered, so that no state is kept and a
+// second GPU of the process gets it too.
+template <int MODE, int D>
+hipError_t prepare_attn_t(bool sparse) {
+  constexpr int W = pipe_waves<MODE, D>();
+  using RG = Ring<MODE, D, W>;
+  const auto kernel = sparse ? &attn_pipe_kernel<MODE, D, W, true> : &attn_pipe_kernel<MODE, D, W, false>;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             sparse ? RG::SPARSE_BYTES : RG::BYTES);
 }
 
 }  // namespace
@@ -660,6 +664,19 @@ hipError_t launch_attn(int mode, const TensorArg& q, const TensorArg& k, const Q
   if (mode == 1) return launch_attn_t<1, 64>(a, s);
   return launch_attn_t<2, 64>(a, s);
 }
+
+hipError_t prepare_attn(int mode, int d, bool sparse) {
+  if (d == 128) {
+    if (mode == 0) return prepare_attn_t<0, 128>(sparse);
+    if (mode == 1) return prepare_attn_t<1, 128>(sparse);
+    return prepare_attn_t<2, 128>(sparse);
+  }
+  if (mode == 0) return prepare_attn_t<0, 64>(sparse);
+  if (mode == 1) return prepare_attn_t<1, 64>(sparse);
+  return prepare_attn_t<2, 64>(sparse);
+}
+
+int attn_rows_per_workgroup() { return 4 * kRowsPerWave; }
 
 hipError_t launch_debug_qk(const QuantArg& qa, int b, int h, int q0, int nq, int k0, int nk, int32_t* out,
                            hipStream_t s) {

@@ -494,15 +494,14 @@ hipError_t launch_linear_t(const LinearArg& p, hipStream_t s) {
   using G = LinGeo<A8, WR>;
   const int mtiles = (p.M + G::TM - 1) / G::TM, ntiles = (p.N + kLinBlk - 1) / kLinBlk;
   const size_t bytes = G::BYTES + (size_t)G::HALVES * (p.K / kLinBlk) * sizeof(float);
-  static bool configured = false;
-  if (!configured) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_kernel<A8, WR>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, kLinLdsMax);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
   linear_kernel<A8, WR><<<(unsigned)(mtiles * ntiles), G::THREADS, bytes, s>>>(p);
   return hipGetLastError();
+}
+
+template <bool A8, int WR>
+hipError_t prepare_linear_t() {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_kernel<A8, WR>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, kLinLdsMax);
 }
 
 }  // namespace
@@ -519,6 +518,14 @@ hipError_t launch_codes_to_bf16(const int8_t* codes, uint16_t* out, int64_t n, h
   const int64_t blocks = std::min<int64_t>((n16 + kLinThreads - 1) / kLinThreads, 8192);
   codes_to_bf16_kernel<<<(unsigned)std::max<int64_t>(blocks, 1), kLinThreads, 0, s>>>(codes, out, n16);
   return hipGetLastError();
+}
+
+// The dynamic LDS limit of every GEMM variant a call may launch, set on the current device before anything is
+// enqueued (on every call: no state is kept, and each GPU of the process gets it).
+hipError_t prepare_linear(bool w8a8) {
+  if (w8a8) return prepare_linear_t<true, 2>();
+  const hipError_t e = prepare_linear_t<false, 4>();
+  return e != hipSuccess ? e : prepare_linear_t<false, 2>();
 }
 
 hipError_t launch_linear(bool w8a8, const LinearArg& p, hipStream_t s) {

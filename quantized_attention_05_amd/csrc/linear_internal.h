@@ -31,5 +31,7 @@ hipError_t launch_quant_blocks(const uint16_t* x, int rows, int cols, int64_t ld
                                hipStream_t s);
 hipError_t launch_codes_to_bf16(const int8_t* codes, uint16_t* out, int64_t n, hipStream_t s);
 hipError_t launch_linear(bool w8a8, const LinearArg& p, hipStream_t s);
+// Per-call set-up of the GEMM kernels a call may launch (their dynamic LDS limit); enqueues nothing.
+hipError_t prepare_linear(bool w8a8);
 
 }  // namespace sattn

@@ -39,6 +39,11 @@ struct QuantArg {
   uint16_t* v_t;
 };
 
+// Per-call set-up of the attention kernel a call will launch (its dynamic LDS limit); enqueues nothing.
+hipError_t prepare_attn(int mode, int d, bool sparse);
+// Query rows of one attention workgroup (the grid has ceil(Nq / rows) * H * B workgroups).
+int attn_rows_per_workgroup();
+
 // Launchers (enqueue only; return hipGetLastError()).
 hipError_t launch_quant_q(const TensorArg& q, const QuantArg& qa, hipStream_t s);
 hipError_t launch_kv_stats(const TensorArg& k, const TensorArg& v, bool with_v, const QuantArg& qa, float* ksum,

@@ -167,13 +167,43 @@ def _ref(t):
 
 # ------------------------------------------------------------------------------------- torch marshalling
 def tensor_desc(t: torch.Tensor | None) -> sattn_tensor | None:
-    """sattn_tensor for a 4-D bf16 device tensor indexed [B, H, N, d] (any strides with d contiguous)."""
+    """sattn_tensor for a 4-D bf16 GPU tensor indexed [B, H, N, d] (any strides with d contiguous)."""
     if t is None:
         return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("expected a GPU tensor: the kernels dereference its pointer on the device")
     if t.dtype != torch.bfloat16 or t.dim() != 4 or t.stride(3) != 1:
         raise ValueError("expected a 4-D bf16 tensor [B, H, N, d] with contiguous channels")
     B, H, N, d = t.shape
     return sattn_tensor(t.data_ptr(), B, H, N, d, t.stride(0), t.stride(1), t.stride(2))
+
+
+def _same_device(name: str, *tensors) -> torch.device:
+    """The one GPU every given tensor lives on (None entries are skipped); ValueError before any C call otherwise."""
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name}: every tensor must be a GPU tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name}: tensors on {dev} and {t.device}; all must share one GPU")
+    if dev is None:
+        raise ValueError(f"{name}: no GPU tensor given")
+    return dev
+
+
+def _workspace(name: str, ws, need: int, dev: torch.device) -> torch.Tensor:
+    """The caller's workspace (a uint8 GPU tensor on `dev`, contiguous, at least `need` bytes) or a new one."""
+    if ws is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or ws.device != dev:
+        raise ValueError(f"{name}: the workspace must be a GPU tensor on {dev}")
+    if ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise ValueError(f"{name}: the workspace must be a contiguous uint8 tensor")
+    return ws
 
 
 def _stream() -> int:
@@ -186,13 +216,14 @@ def _resolve(sm_scale, d):
 
 def fwd(q, k, v, mode=SATTN_MODE_I8_FP8, sm_scale=None, blk_q=128, blk_k=64, out=None, workspace=None):
     """Self-attention through sattn_fwd.  q, k, v: [B, H, N, d] bf16 on the GPU.  Returns O like q."""
+    dev = _same_device("fwd", q, k, v, out)
     B, H, Nq, d = q.shape
     Nkv = k.shape[2]
     o = torch.empty_like(q) if out is None else out
     need = sattn_workspace_bytes(B, H, Nq, Nkv, d, blk_q, blk_k, mode)
     if need == 0:
         raise SattnError(SATTN_ERR_UNSUPPORTED, "sattn_workspace_bytes")
-    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws = _workspace("fwd", workspace, need, dev)
     sattn_fwd(tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(o), _resolve(sm_scale, d), mode, blk_q, blk_k,
               ws.data_ptr(), ws.numel(), _stream())
     return o
@@ -211,17 +242,16 @@ def fwd_block_sparse(q, k, v, mask, mode=SATTN_MODE_I8_FP8, sm_scale=None, blk_q
                      workspace=None):
     """Block-sparse self-attention through sattn_fwd_block_sparse.  mask: uint8 (nonzero = keep) on the GPU, shaped
     mask_shape(B, H, Nq, Nkv), contiguous.  Returns O like q."""
+    dev = _same_device("fwd_block_sparse", q, k, v, mask, out)
     B, H, Nq, d = q.shape
     Nkv = k.shape[2]
     if tuple(mask.shape) != mask_shape(B, H, Nq, Nkv) or mask.dtype != torch.uint8 or not mask.is_contiguous():
         raise SattnError(SATTN_ERR_INVALID_ARG, "fwd_block_sparse: mask shape/dtype/layout")
-    if mask.device != q.device:
-        raise SattnError(SATTN_ERR_INVALID_ARG, "fwd_block_sparse: mask must be on the GPU of q")
     o = torch.empty_like(q) if out is None else out
     need = sattn_workspace_bytes(B, H, Nq, Nkv, d, blk_q, blk_k, mode)
     if need == 0:
         raise SattnError(SATTN_ERR_UNSUPPORTED, "sattn_workspace_bytes")
-    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws = _workspace("fwd_block_sparse", workspace, need, dev)
     sattn_fwd_block_sparse(tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(o), mask.data_ptr(),
                            _resolve(sm_scale, d), mode, blk_q, blk_k, ws.data_ptr(), ws.numel(), _stream())
     return o
@@ -229,13 +259,14 @@ def fwd_block_sparse(q, k, v, mask, mode=SATTN_MODE_I8_FP8, sm_scale=None, blk_q
 
 def cross_fwd(q, k, v, mode=SATTN_MODE_BF16, sm_scale=None, out=None, workspace=None):
     """Cross-attention through sattn_cross_fwd (short key sequence).  Returns O like q."""
+    dev = _same_device("cross_fwd", q, k, v, out)
     B, H, Nq, d = q.shape
     Nkv = k.shape[2]
     o = torch.empty_like(q) if out is None else out
     need = sattn_workspace_bytes(B, H, Nq, Nkv, d, 128, 64, mode)
     if need == 0:
         raise SattnError(SATTN_ERR_UNSUPPORTED, "sattn_workspace_bytes")
-    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws = _workspace("cross_fwd", workspace, need, dev)
     sattn_cross_fwd(tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(o), _resolve(sm_scale, d), mode,
                     ws.data_ptr(), ws.numel(), _stream())
     return o
@@ -244,8 +275,9 @@ def cross_fwd(q, k, v, mode=SATTN_MODE_BF16, sm_scale=None, out=None, workspace=
 def error_stats(a, ref):
     """Per-head fp64 sums [sum (a-ref)^2, sum ref^2, sum a*ref, sum a^2] of two [B, H, N, d] bf16 GPU tensors
     through sattn_error_stats.  Returns a [B, H, 4] float64 GPU tensor."""
+    dev = _same_device("error_stats", a, ref)
     B, H = a.shape[0], a.shape[1]
-    out = torch.empty((B, H, 4), dtype=torch.float64, device=a.device)
+    out = torch.empty((B, H, 4), dtype=torch.float64, device=dev)
     sattn_error_stats(tensor_desc(a), tensor_desc(ref), out.data_ptr(), _stream())
     return out
 
@@ -254,6 +286,8 @@ class Quantized:
     """Quantized operands in one device buffer, with torch views of each array (see sattn_quant)."""
 
     def __init__(self, B, H, Nq, Nkv, d, blk_q, mode, device, blk_k=64):
+        if torch.device(device).type != "cuda":
+            raise ValueError("Quantized: the code buffer must live on a GPU")
         self.shape = (B, H, Nq, Nkv, d, blk_q, blk_k, mode)
         nbytes = sattn_quant_bytes(B, H, Nq, Nkv, d, blk_q, blk_k, mode)
         if nbytes == 0:
@@ -286,21 +320,23 @@ class Quantized:
 
 def quantize(q, k, v, mode=SATTN_MODE_I8_FP8, blk_q=128, quant: Quantized | None = None):
     """Run sattn_quantize; returns a ``Quantized`` holding the codes/scales (device tensors)."""
+    dev = _same_device("quantize", q, k, v, None if quant is None else quant.buf)
     B, H, Nq, d = q.shape
     Nkv = k.shape[2]
-    qz = quant if quant is not None else Quantized(B, H, Nq, Nkv, d, blk_q, mode, q.device)
+    qz = quant if quant is not None else Quantized(B, H, Nq, Nkv, d, blk_q, mode, dev)
     sb = sattn_quantize_scratch_bytes(B, H, Nkv, d, mode)
-    scratch = torch.empty(max(sb, 1), dtype=torch.uint8, device=q.device)
+    scratch = torch.empty(max(sb, 1), dtype=torch.uint8, device=dev)
     sattn_quantize(tensor_desc(q), tensor_desc(k), tensor_desc(v), mode, qz.desc, scratch.data_ptr(), sb, _stream())
     qz._scratch = scratch  # keep alive until the stream has used it
     return qz
 
 
-def fwd_quantized(qz: Quantized, q=None, k=None, sm_scale=None, out=None, Nq_like=None):
+def fwd_quantized(qz: Quantized, q=None, k=None, sm_scale=None, out=None):
     """Attention on prepared operands through sattn_fwd_quantized."""
+    dev = _same_device("fwd_quantized", qz.buf, q, k, out)
     B, H, Nq, Nkv, d, blk_q, blk_k, mode = qz.shape
     if out is None:
-        out = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device=qz.buf.device)
+        out = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device=dev)
     sattn_fwd_quantized(tensor_desc(q), tensor_desc(k), qz.desc, tensor_desc(out), _resolve(sm_scale, d), mode,
                         _stream())
     return out

@@ -219,3 +219,36 @@ def test_linear_binding_validates_before_the_call(S):
                  lambda: S.linear_quantized(wq, sw, wq.to(torch.int16), sw)):
         with pytest.raises(ValueError):
             call()
+
+
+def test_attention_binding_validates_devices_before_the_call(S, monkeypatch):
+    """The torch-level attention entry points raise ValueError for host tensors, host workspaces and host masks before
+    any compute call reaches the C ABI (a host pointer handed to a kernel would fault the GPU)."""
+    import torch
+
+    def no_call(*a, **k):
+        raise AssertionError("a compute entry point was reached")
+
+    for name in ("sattn_fwd", "sattn_cross_fwd", "sattn_fwd_block_sparse", "sattn_quantize", "sattn_fwd_quantized",
+                 "sattn_error_stats", "sattn_debug_qk_int32"):
+        monkeypatch.setattr(S, name, no_call)
+    q = torch.zeros((1, 2, 64, 64), dtype=torch.bfloat16)
+    mask = torch.ones(S.mask_shape(1, 2, 64, 64), dtype=torch.uint8)
+    calls = [
+        lambda: S.fwd(q, q, q),
+        lambda: S.fwd(q, q, q, mode=0),
+        lambda: S.cross_fwd(q, q, q),
+        lambda: S.fwd_block_sparse(q, q, q, mask),
+        lambda: S.quantize(q, q, q),
+        lambda: S.error_stats(q, q),
+        lambda: S.tensor_desc(q),
+        lambda: S.Quantized(1, 2, 64, 64, 64, 64, 2, "cpu"),
+    ]
+
+    class FakeQuant:  # a Quantized whose buffer sits in host memory
+        shape = (1, 2, 64, 64, 64, 64, 64, 2)
+        buf = torch.zeros(16, dtype=torch.uint8)
+    calls.append(lambda: S.fwd_quantized(FakeQuant()))
+    for call in calls:
+        with pytest.raises(ValueError):
+            call()
