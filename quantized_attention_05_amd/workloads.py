@@ -63,7 +63,11 @@ WORKLOADS = {
     for w in [
         Workload("tiny", 1, 2, 256, 256, 64, 64, 64, "tiny", 0, (1,)),
         Workload("wan1.3b-480p", 1, 12, 32760, 32760, 128, 128, 64, "outlier", 1, (1,)),
-        Workload("wan14b-480p", 1, 40, 32760, 32760, 128, 128, 64, "outlier", 2, (0, 1, 2)),
+        # Wan-14B 480p: "the same distributions as config 1" read with 1-based numbering, i.e. the tiny recipe
+        # (U(-4, 4) channel offsets, K channel 0 zeroed) at the 14B shape ...
+        Workload("wan14b-480p", 1, 40, 32760, 32760, 128, 128, 64, "tiny", 2, (0, 1, 2)),
+        # ... and read with 0-based numbering, the Wan-1.3B recipe (N(0, 3^2) offsets, 4 outlier channels x10)
+        Workload("wan14b-480p-outlier", 1, 40, 32760, 32760, 128, 128, 64, "outlier", 202, (0, 1, 2)),
         Workload("wan14b-720p", 1, 40, 75600, 75600, 128, 128, 64, "zeroblk", 3, (2,)),
         # one self-attention layer of the layer-selective pass (layer l uses seed 1000 + l) ...
         Workload("layersel-720p-self", 1, 40, 75600, 75600, 128, 128, 64, "plain", 1000, (0, 2)),

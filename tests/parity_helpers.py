@@ -14,8 +14,18 @@ import oracle
 from quantized_attention_05_amd import sattn
 from quantized_attention_05_amd import workloads as wl
 
-REL_L2_GATE = 2e-3   # GPU output vs the oracle's step-by-step emulation
+REL_L2_GATE = 2e-3   # GPU output vs the oracle's step-by-step emulation, pooled over the compared rows
 COS_GATE = 0.999     # GPU output vs fp64 exact attention, where the emulation itself reaches it
+# Per query row (rel-L2 of that row vs the emulation), so that a wrong row cannot hide inside the pooled figure.  A
+# row legitimately differs by bf16 rounding ties of its outputs (at most one ulp each, i.e. 2^-8 relative) and by the
+# rare P roundings that the hardware exp2 and the MFMA summation order flip.  One E4M3 step of the weight w_j of key j
+# is at most w_j / 8, and w_j <= 1/2 for every key whose P is rounded at all (the running max of its tile has P = 448
+# exactly), so one flip moves a row by at most |v_j| / 16; with N_eff effective keys it moves it by about
+# 1 / (8 sqrt(N_eff)) of its norm: 7e-4 at 75 600 keys, 7e-3 at 1 000.  Hence every row within ROW_GATE, and all but
+# max(1, ROW_FRAC of the rows) within ROW_SOFT: a systematic fault (a lane, a tile, a block scale) moves many rows.
+ROW_GATE = 2e-2
+ROW_SOFT = 5e-3
+ROW_FRAC = 0.01
 
 
 def say(*a):
@@ -97,14 +107,42 @@ def metrics(gpu: np.ndarray, E: np.ndarray, R: np.ndarray):
     return rel, cos, cos_e
 
 
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values at |x| (the normal range; 2^-133 below it)."""
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(ax, 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+def row_metrics(gpu: np.ndarray, E: np.ndarray):
+    """Per query row (last axis = channels): rel-L2 of the row vs the emulation (a row of zeros in E compares its
+    absolute norm), and the largest element difference in bf16 ulps of the emulation's value."""
+    gpu = gpu.astype(np.float64).reshape(-1, gpu.shape[-1])
+    E = E.astype(np.float64).reshape(-1, E.shape[-1])
+    num = np.linalg.norm(gpu - E, axis=1)
+    den = np.linalg.norm(E, axis=1)
+    rel = np.where(den > 0, num / np.maximum(den, 1e-300), num)
+    ulps = np.abs(gpu - E) / bf16_ulp(E)
+    return rel, ulps
+
+
 def check_output(gpu_rows: np.ndarray, E: np.ndarray, R: np.ndarray, label: str):
     assert np.all(np.isfinite(gpu_rows)), f"{label}: non-finite output"
     rel, cos, cos_e = metrics(gpu_rows, E, R)
-    say(f"  {label}: rel-L2 vs emulation {rel:.3e}, cos vs fp64 {cos:.6f} (emulation {cos_e:.6f})")
+    rrel, ulps = row_metrics(gpu_rows, E)
+    worst = int(np.argmax(rrel))
+    say(f"  {label}: rel-L2 vs emulation {rel:.3e}, cos vs fp64 {cos:.6f} (emulation {cos_e:.6f}); worst row "
+        f"{worst} rel-L2 {rrel[worst]:.3e}, max |diff| {ulps.max():.0f} bf16 ulp, "
+        f"{np.count_nonzero(ulps.max(axis=1) > 1)} of {rrel.size} rows beyond 1 ulp")
     assert rel <= REL_L2_GATE, f"{label}: rel-L2 {rel:.3e} > {REL_L2_GATE}"
-    # the cosine gate applies where the method itself (the emulation) reaches it
+    assert rrel[worst] <= ROW_GATE, f"{label}: row {worst} rel-L2 {rrel[worst]:.3e} > {ROW_GATE}"
+    n_soft = int(np.count_nonzero(rrel > ROW_SOFT))
+    allowed = max(1, int(ROW_FRAC * rrel.size))
+    assert n_soft <= allowed, f"{label}: {n_soft} rows beyond rel-L2 {ROW_SOFT} (at most {allowed})"
+    # the cosine gate applies where the method itself (the emulation) reaches it; elsewhere the GPU must be as close
+    # to exact attention as the emulation is
     if cos_e >= COS_GATE:
-        assert cos >= COS_GATE - 1e-4, f"{label}: cosine {cos:.6f}"
+        assert cos >= COS_GATE, f"{label}: cosine {cos:.6f} < {COS_GATE}"
     else:
         assert cos >= cos_e - 1e-4, f"{label}: cosine {cos:.6f} below the emulation's {cos_e:.6f}"
     return rel, cos

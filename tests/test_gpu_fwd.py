@@ -80,6 +80,9 @@ LARGE = [
     ("wan14b-480p", W["wan14b-480p"], 0),
     ("wan14b-480p", W["wan14b-480p"], 1),
     ("wan14b-480p", W["wan14b-480p"], 2),
+    ("wan14b-480p-outlier", W["wan14b-480p-outlier"], 0),
+    ("wan14b-480p-outlier", W["wan14b-480p-outlier"], 1),
+    ("wan14b-480p-outlier", W["wan14b-480p-outlier"], 2),
     ("wan14b-720p", W["wan14b-720p"], 2),
     ("wan14b-720p", W["wan14b-720p"], 1),
     ("wan14b-720p", W["wan14b-720p"], 0),
@@ -179,3 +182,48 @@ def test_layer_selective_sequence_has_no_state():
         alone = sattn.fwd(q, k, v, mode=m, sm_scale=w.sm_scale)
         torch.cuda.synchronize()
         assert torch.equal(o.view(torch.int16), alone.view(torch.int16))
+
+
+# ------------------------------------------------------------------------------------- prepared operands
+QUANTIZED = [
+    ("tiny", W["tiny"], 64),
+    ("ragged-d128", wl.scaled(W["wan14b-720p"], name="ragged-d128", H=3, Nq=1000, Nkv=1000, seed=11), 128),
+    ("ragged-d64", wl.scaled(W["tiny"], name="ragged-d64", H=2, Nq=333, Nkv=197, seed=12), 64),
+    ("ragged-q64-d128", wl.scaled(W["wan1.3b-480p"], name="ragged-q64-d128", H=2, Nq=700, Nkv=650, seed=13), 64),
+]
+
+
+def run_fwd_quantized(w, mode, blk_q, q, k, v):
+    qz = sattn.quantize(q, k, v, mode=mode, blk_q=blk_q)
+    o = sattn.fwd_quantized(qz, q if mode == 0 else None, k if mode == 0 else None, sm_scale=w.sm_scale)
+    torch.cuda.synchronize()
+    return o
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("name,w,blk_q", QUANTIZED, ids=[c[0] for c in QUANTIZED])
+def test_fwd_quantized_matches_fwd_and_oracle(name, w, blk_q, mode):
+    """sattn_quantize + sattn_fwd_quantized (the attention kernel on prepared operands, as the benchmark times it)
+    gives exactly the bits of the drop-in sattn_fwd, and every row passes the oracle's gate."""
+    say(f"[fwd_quantized] {name} mode {mode}")
+    q, k, v = device_inputs(w)
+    o = run_fwd_quantized(w, mode, blk_q, q, k, v)
+    ref = sattn.fwd(q, k, v, mode=mode, sm_scale=w.sm_scale, blk_q=blk_q)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), ref.view(torch.int16)), f"{name} mode {mode}: differs from sattn_fwd"
+    compare(w, mode, blk_q, o, label=f"{name} prepared")
+
+
+@pytest.mark.parametrize("mode", [2, 1, 0])
+def test_fwd_quantized_full_size(mode):
+    """The headline 720p shape through sattn_fwd_quantized: bit-identical to sattn_fwd on the whole output, and the
+    sampled rows of three heads pass the oracle's gate."""
+    w = W["wan14b-720p"]
+    say(f"[fwd_quantized full] {w.name} mode {mode}")
+    q, k, v = device_inputs(w)
+    o = run_fwd_quantized(w, mode, w.blk_q, q, k, v)
+    ref = sattn.fwd(q, k, v, mode=mode, sm_scale=w.sm_scale, blk_q=w.blk_q)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), ref.view(torch.int16)), f"mode {mode}: differs from sattn_fwd"
+    del ref
+    compare(w, mode, w.blk_q, o, heads=sample_heads(w.H), rows=sample_rows(w.Nq, w.blk_q), label=f"{w.name} prepared")

@@ -48,6 +48,15 @@ def check(y_gpu_bits, y, mag, K, w8a8, label):
     assert np.all(err <= lim), f"{label}: {np.sum(err > lim)} elements outside the bound (worst ratio {worst:.3f})"
 
 
+def weight_codes(w_host: torch.Tensor, wq: torch.Tensor, sw: torch.Tensor):
+    """The oracle's own codes and block scales of a weight, after checking that the GPU's equal them bit for bit; the
+    references below are built from these, never from the GPU's."""
+    wq_o, sw_o = oracle.quant_blocks(bits(w_host))
+    assert np.array_equal(wq.cpu().numpy(), wq_o), "weight codes differ from the oracle's"
+    assert np.array_equal(sw.cpu().numpy().view(np.uint32), sw_o.view(np.uint32)), "weight scales differ"
+    return wq_o, sw_o
+
+
 def cosine(a, b):
     return float(np.sum(a * b) / np.sqrt(np.sum(a * a) * np.sum(b * b)))
 
@@ -87,12 +96,13 @@ def test_linear_small(name, M, N, K, with_bias):
     xd, wd = x.cuda(), w.cuda()
     bd = None if b is None else b.cuda()
     wq, sw = sattn.quantize_blocks(wd)
+    wq_o, sw_o = weight_codes(w, wq, sw)
     bb = None if b is None else bits(b)
     exact = val(bits(x)) @ val(bits(w)).T + (0.0 if b is None else val(bb))
     # W8A8
     y8 = sattn.linear(xd, wq, sw, bd, mode=sattn.SATTN_LINEAR_W8A8)
     xq, sx = oracle.quant_blocks(bits(x))
-    ref, mag = oracle.linear_w8a8(xq, sx, wq.cpu().numpy(), sw.cpu().numpy(), bb)
+    ref, mag = oracle.linear_w8a8(xq, sx, wq_o, sw_o, bb)
     check(bits(y8), ref, mag, K, True, f"{name} W8A8")
     close_to_exact(val(bits(y8)), ref, exact, f"{name} W8A8")
     # the same on codes prepared separately
@@ -101,7 +111,7 @@ def test_linear_small(name, M, N, K, with_bias):
     assert torch.equal(y8q.view(torch.int16), y8.view(torch.int16))
     # W8A16
     y16 = sattn.linear(xd, wq, sw, bd, mode=sattn.SATTN_LINEAR_W8A16)
-    ref16, mag16 = oracle.linear_w8a16(bits(x), wq.cpu().numpy(), sw.cpu().numpy(), bb)
+    ref16, mag16 = oracle.linear_w8a16(bits(x), wq_o, sw_o, bb)
     check(bits(y16), ref16, mag16, K, False, f"{name} W8A16")
     close_to_exact(val(bits(y16)), ref16, exact, f"{name} W8A16")
 
@@ -112,8 +122,9 @@ def test_linear_w8a16_long_k():
     M, N, K = 300, 16, 2049 * BLK
     x, w, b = wl.linear_host_inputs(M, N, K, seed=74)
     wq, sw = sattn.quantize_blocks(w.cuda())
+    wq_o, sw_o = weight_codes(w, wq, sw)
     y = sattn.linear(x.cuda(), wq, sw, b.cuda(), mode=sattn.SATTN_LINEAR_W8A16)
-    ref, mag = oracle.linear_w8a16(bits(x), wq.cpu().numpy(), sw.cpu().numpy(), bits(b))
+    ref, mag = oracle.linear_w8a16(bits(x), wq_o, sw_o, bits(b))
     check(bits(y), ref, mag, K, False, "long-K W8A16")
 
 
@@ -126,8 +137,9 @@ def test_linear_w8a16_wide_row_stride():
     xd = torch.zeros((M, ldx), dtype=torch.bfloat16, device="cuda")
     xd[:, :K] = x.cuda()
     wq, sw = sattn.quantize_blocks(w.cuda())
+    wq_o, sw_o = weight_codes(w, wq, sw)
     y = sattn.linear(xd[:, :K], wq, sw, b.cuda(), mode=sattn.SATTN_LINEAR_W8A16)
-    ref, mag = oracle.linear_w8a16(bits(x), wq.cpu().numpy(), sw.cpu().numpy(), bits(b))
+    ref, mag = oracle.linear_w8a16(bits(x), wq_o, sw_o, bits(b))
     check(bits(y), ref, mag, K, False, "wide-stride W8A16")
     del xd
 
