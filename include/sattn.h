@@ -37,7 +37,8 @@
  *   - The caller owns every buffer.  The library keeps no state between calls (no flags, caches or handles;
  *     per-kernel launch attributes are set on the current device by every call), so it is re-entrant and
  *     serves every GPU of a process alike; concurrent calls need distinct workspaces and outputs.  Outputs
- *     must not alias inputs.
+ *     must not alias inputs.  The one exception is sattn_fwd_noalloc, whose workspace is the library's own
+ *     per-GPU array (its device address is looked up once per device and kept).
  *   - Errors: arguments are checked on the host before any launch.  A bad argument returns
  *     SATTN_ERR_INVALID_ARG, a valid but unsupported shape SATTN_ERR_UNSUPPORTED, a too small workspace
  *     SATTN_ERR_WORKSPACE; in these cases nothing has been enqueued.  SATTN_ERR_HIP reports a failure of
@@ -151,6 +152,20 @@ sattn_status sattn_fwd_quantized(const sattn_tensor* q, const sattn_tensor* k, c
 sattn_status sattn_fwd(const sattn_tensor* q, const sattn_tensor* k, const sattn_tensor* v, const sattn_tensor* o,
                        float sm_scale, int mode, int blk_q, int blk_k, void* ws, size_t ws_bytes,
                        sattn_stream_t stream);
+
+/* sattn_fwd without a caller workspace, for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The workspace is a fixed array of
+ * SATTN_NOALLOC_SCRATCH_BYTES bytes inside the library: every GPU the library runs on holds its own copy until the
+ * process ends; the call itself allocates nothing.  Arguments and results as sattn_fwd;
+ * a shape whose sattn_workspace_bytes exceeds SATTN_NOALLOC_SCRATCH_BYTES returns SATTN_ERR_WORKSPACE (nothing is
+ * enqueued).  Every call on one GPU shares that GPU's array and leaves its contents behind (nothing in it needs to
+ * start at zero): calls that overlap on one GPU, on concurrent streams or from several host threads, race and must
+ * be serialised by the caller.  256 MiB holds, e.g., every mode of a Wan-1.3B 480p self-attention call (H 12,
+ * N 32 760, d 128) and a 720p cross-attention call over 769 keys in mode 0. */
+#define SATTN_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+sattn_status sattn_fwd_noalloc(const sattn_tensor* q, const sattn_tensor* k, const sattn_tensor* v,
+                               const sattn_tensor* o, float sm_scale, int mode, int blk_q, int blk_k,
+                               sattn_stream_t stream);
 
 /* Cross-attention of the video tokens (Nq long) over a short key sequence (Nkv small: e.g. 512 text +
  * 257 image tokens of a Wan I2V block, one softmax over their concatenation).  Same arithmetic and

@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["api.cpp", "quant.hip", "attn.hip", "probe.hip", "linear.hip"]
+SOURCES = ["api.cpp", "quant.hip", "attn.hip", "probe.hip", "linear.hip", "noalloc.hip"]
 LIB = os.path.join(HERE, "libsattn.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

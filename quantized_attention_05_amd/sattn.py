@@ -67,6 +67,7 @@ SYMBOLS = [
     ("sattn_quantize", _I, [_TP, _TP, _TP, _I, _QP, _P, _SZ, _P]),
     ("sattn_fwd_quantized", _I, [_TP, _TP, _QP, _TP, ctypes.c_float, _I, _P]),
     ("sattn_fwd", _I, [_TP, _TP, _TP, _TP, ctypes.c_float, _I, _I, _I, _P, _SZ, _P]),
+    ("sattn_fwd_noalloc", _I, [_TP, _TP, _TP, _TP, ctypes.c_float, _I, _I, _I, _P]),
     ("sattn_cross_fwd", _I, [_TP, _TP, _TP, _TP, ctypes.c_float, _I, _P, _SZ, _P]),
     ("sattn_fwd_block_sparse", _I, [_TP, _TP, _TP, _TP, _P, ctypes.c_float, _I, _I, _I, _P, _SZ, _P]),
     ("sattn_error_stats", _I, [_TP, _TP, _P, _P]),
@@ -137,6 +138,11 @@ def sattn_fwd_quantized(q, k, qk: sattn_quant, o, sm_scale, mode, stream: int):
 def sattn_fwd(q, k, v, o, sm_scale, mode, blk_q, blk_k, ws: int, ws_bytes: int, stream: int):
     _check(lib().sattn_fwd(_ref(q), _ref(k), _ref(v), _ref(o), float(sm_scale), mode, blk_q, blk_k,
                            ctypes.c_void_p(ws), ws_bytes, ctypes.c_void_p(stream)), "sattn_fwd")
+
+
+def sattn_fwd_noalloc(q, k, v, o, sm_scale, mode, blk_q, blk_k, stream: int):
+    _check(lib().sattn_fwd_noalloc(_ref(q), _ref(k), _ref(v), _ref(o), float(sm_scale), mode, blk_q, blk_k,
+                                   ctypes.c_void_p(stream)), "sattn_fwd_noalloc")
 
 
 def sattn_cross_fwd(q, k, v, o, sm_scale, mode, ws: int, ws_bytes: int, stream: int):
@@ -227,6 +233,18 @@ def fwd(q, k, v, mode=SATTN_MODE_I8_FP8, sm_scale=None, blk_q=128, blk_k=64, out
     sattn_fwd(tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(o), _resolve(sm_scale, d), mode, blk_q, blk_k,
               ws.data_ptr(), ws.numel(), _stream())
     return o
+
+
+NOALLOC_SCRATCH_BYTES = 256 << 20  # SATTN_NOALLOC_SCRATCH_BYTES
+
+
+def fwd_noalloc(q, k, v, out, mode=SATTN_MODE_I8_FP8, sm_scale=None, blk_q=128, blk_k=64):
+    """Self-attention through sattn_fwd_noalloc: the workspace is the library's own per-GPU array, so the call allocates
+    nothing; the caller passes the output `out` ([B, H, Nq, d] bf16 on the GPU of q)."""
+    _same_device("fwd_noalloc", q, k, v, out)
+    sattn_fwd_noalloc(tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(out), _resolve(sm_scale, q.shape[3]),
+                      mode, blk_q, blk_k, _stream())
+    return out
 
 
 MASK_QBLK = 128  # query rows per block-sparse mask row (SATTN_MASK_QBLK)

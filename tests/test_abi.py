@@ -200,6 +200,20 @@ def test_argument_errors_are_caught_on_the_host(S):
     assert L.sattn_debug_qk_int32(byref(qd), 0, 0, 0, 4, 0, 0, out, None) == S.SATTN_ERR_INVALID_ARG
 
 
+def test_noalloc_refuses_shapes_beyond_its_array(S):
+    """sattn_fwd_noalloc checks the workspace its shape needs against the library's fixed array on the host, before
+    any device call: one head of the 720p shape fits, 40 do not (fake pointers, never dereferenced)."""
+    L = S.lib()
+    P = 1 << 24
+    N, d = 75600, 128
+    assert S.sattn_workspace_bytes(1, 1, N, N, d, 128, 64, 2) <= S.NOALLOC_SCRATCH_BYTES
+    assert S.sattn_workspace_bytes(1, 40, N, N, d, 128, 64, 2) > S.NOALLOC_SCRATCH_BYTES
+    t = S.sattn_tensor(P, 1, 40, N, d, 40 * N * d, N * d, d)
+    st = L.sattn_fwd_noalloc(ctypes.byref(t), ctypes.byref(t), ctypes.byref(t), ctypes.byref(t), 0.0, 2, 128, 64, None)
+    assert st == S.SATTN_ERR_WORKSPACE
+    assert L.sattn_fwd_noalloc(None, None, None, None, 0.0, 2, 128, 64, None) == S.SATTN_ERR_INVALID_ARG
+
+
 def test_binding_raises(S):
     with pytest.raises(S.SattnError) as ei:
         S.sattn_fwd(None, None, None, None, 0.0, 2, 64, 64, 0, 0, 0)
