@@ -270,22 +270,31 @@ def linear_layers(args):
 
 
 def cpu_baseline(w, mode: int, budget_s: float):
-    """The oracle, as it stands, on a bounded sample: quantize one head in full, then emulate query blocks of
-    that head until about `budget_s` seconds of CPU time are spent.  Extrapolated linearly to the whole call
+    """The oracle, as it stands, on a bounded sample: heads {0, H/2, H-1} are quantized in full, then query blocks
+    {first, middle, last} of each of them are emulated against all keys, followed by further blocks of the three
+    heads in turn, until about `budget_s` seconds of CPU time are spent.  Extrapolated linearly to the whole call
     (H heads x all query rows) and reported as effective TOPS."""
     import numpy as np
 
     import oracle
     from quantized_attention_05_amd import workloads as wl
 
-    q, k, v = (wl.bits(t) for t in wl.head_inputs(w, 0, 0))
-    t0 = time.perf_counter()
-    quant = oracle.quantize_head(q, k, v, w.blk_q, w.blk_k, mode) if mode != 0 else None
-    t_quant = time.perf_counter() - t0
+    heads = sorted({0, w.H // 2, w.H - 1})
     nqb = -(-w.Nq // w.blk_q)
-    order = [0, nqb - 1] + [int(i) for i in np.linspace(1, nqb - 2, 64).astype(int)]
-    rows_done, t_attn, blocks = 0, 0.0, []
-    for blk in order:
+    t_quant, data = 0.0, []
+    for h in heads:
+        q, k, v = (wl.bits(t) for t in wl.head_inputs(w, 0, h))
+        t0 = time.perf_counter()
+        quant = oracle.quantize_head(q, k, v, w.blk_q, w.blk_k, mode) if mode != 0 else None
+        t_quant += time.perf_counter() - t0
+        data.append((q, k, v, quant))
+    # blocks {0, middle, last} of every sampled head first, then spread blocks of each head in turn
+    extra = sorted({int(i) for i in np.linspace(1, nqb - 2, 64).astype(int)})
+    order = [(hi, blk) for blk in (0, nqb // 2, nqb - 1) for hi in range(len(heads))]
+    order += [(hi, blk) for blk in extra for hi in range(len(heads)) if blk not in (0, nqb // 2, nqb - 1)]
+    rows_done, t_attn, done = 0, 0.0, []
+    for hi, blk in order:
+        q, k, v, quant = data[hi]
         rows = np.arange(blk * w.blk_q, min((blk + 1) * w.blk_q, w.Nq), dtype=np.int32)
         t0 = time.perf_counter()
         if mode == 0:
@@ -296,18 +305,20 @@ def cpu_baseline(w, mode: int, budget_s: float):
                                 quant=quant, v_bf16=v)
         t_attn += time.perf_counter() - t0
         rows_done += rows.size
-        blocks.append(blk)
-        if t_quant + t_attn >= budget_s:
+        done.append((heads[hi], blk))
+        if t_quant + t_attn >= budget_s and len(done) >= 3 * len(heads):
             break
-    t_call = w.H * w.B * (t_quant + t_attn * (w.Nq / rows_done))
+    # per head: its quantization plus all Nq rows at the measured rate
+    t_call = w.H * w.B * (t_quant / len(heads) + t_attn * (w.Nq / rows_done))
     return {
         "value": w.ops / t_call / 1e12,
         "unit": "TOPS",
         "cores": oracle.max_threads(),
         "kind": "oracle",
-        "sample": (f"head 0 of {w.name}: full quantization ({t_quant:.2f} s) + step-by-step emulation of "
-                   f"{rows_done} query rows in {len(blocks)} blocks against all {w.Nkv} keys ({t_attn:.2f} s); "
-                   f"extrapolated to {w.B * w.H} heads x {w.Nq} rows = {t_call:.1f} s per call"),
+        "sample": (f"heads {heads} of {w.name}: full quantization ({t_quant:.2f} s) + step-by-step emulation of "
+                   f"{rows_done} query rows in {len(done)} blocks (first/middle/last of each head, then spread) "
+                   f"against all {w.Nkv} keys ({t_attn:.2f} s); extrapolated to {w.B * w.H} heads x {w.Nq} rows = "
+                   f"{t_call:.1f} s per call"),
         "seconds_measured": round(t_quant + t_attn, 2),
     }
 
