@@ -128,8 +128,10 @@ size_t sattn_quant_bytes(int B, int H, int Nq, int Nkv, int d, int blk_q, int bl
 sattn_status sattn_quant_layout(int B, int H, int Nq, int Nkv, int d, int blk_q, int blk_k, int mode, void* base,
                                 sattn_quant* out);
 
-/* Workspace bytes for sattn_fwd / sattn_cross_fwd (the quantized operands plus the per-64-token
- * partial sums of the K-mean and V-amax passes), or 0 if the shape is invalid. */
+/* Workspace bytes for sattn_fwd / sattn_cross_fwd / sattn_fwd_block_sparse: the quantized K and V operands of
+ * sattn_quant (the Q codes are left out: these calls quantize each Q block inside the attention kernel, with the
+ * same rule and the same codes as sattn_quantize) plus the per-64-token partial sums of the K-mean and V-amax
+ * passes; or 0 if the shape is invalid. */
 size_t sattn_workspace_bytes(int B, int H, int Nq, int Nkv, int d, int blk_q, int blk_k, int mode);
 
 /* Scratch bytes needed by sattn_quantize (per-64-token K partial sums and V partial maxima). */
@@ -147,7 +149,9 @@ sattn_status sattn_quantize(const sattn_tensor* q, const sattn_tensor* k, const 
 sattn_status sattn_fwd_quantized(const sattn_tensor* q, const sattn_tensor* k, const sattn_quant* qk,
                                  const sattn_tensor* o, float sm_scale, int mode, sattn_stream_t stream);
 
-/* Drop-in self-attention: quantize (or transpose V for mode 0) into `ws`, then attend.
+/* Drop-in self-attention: quantize K and V (or transpose V for mode 0) into `ws`, then attend; in modes 1 and 2
+ * the attention kernel quantizes each blk_q-row Q block itself (the codes of sattn_quantize, bit for bit), so the
+ * result equals sattn_quantize + sattn_fwd_quantized exactly.
  * q, o: [B,H,Nq,d]; k, v: [B,H,Nkv,d]; ws: sattn_workspace_bytes(...) bytes of device memory. */
 sattn_status sattn_fwd(const sattn_tensor* q, const sattn_tensor* k, const sattn_tensor* v, const sattn_tensor* o,
                        float sm_scale, int mode, int blk_q, int blk_k, void* ws, size_t ws_bytes,

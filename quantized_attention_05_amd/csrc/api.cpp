@@ -44,14 +44,16 @@ struct Sizes {
   size_t q_codes, q_scales, k_codes, k_scales, k_mean, v_codes, v_scales, v_t, total;
 };
 
-Sizes sizes(int B, int H, int Nq, int Nkv, int d, int blk_q, int mode) {
+// Sizes of the quantized operands.  with_q = false leaves out the Q codes and scales: the drop-in calls quantize Q
+// inside the attention kernel and keep only K and V in the workspace.
+Sizes sizes(int B, int H, int Nq, int Nkv, int d, int blk_q, int mode, bool with_q = true) {
   Sizes s;
   const size_t bh = (size_t)B * H;
   s.nqb = cdiv(Nq, blk_q);
   s.nkb = cdiv(Nkv, kTile);
   const bool quant = mode != SATTN_MODE_BF16;
-  s.q_codes = quant ? align_up(bh * s.nqb * blk_q * d) : 0;
-  s.q_scales = quant ? align_up(bh * s.nqb * sizeof(float)) : 0;
+  s.q_codes = quant && with_q ? align_up(bh * s.nqb * blk_q * d) : 0;
+  s.q_scales = quant && with_q ? align_up(bh * s.nqb * sizeof(float)) : 0;
   s.k_codes = quant ? align_up(bh * (size_t)s.nkb * kTile * d) : 0;
   s.k_scales = quant ? align_up(bh * s.nkb * sizeof(float)) : 0;
   s.k_mean = quant ? align_up(bh * d * sizeof(float)) : 0;
@@ -126,8 +128,10 @@ sattn_status check_quant(const sattn_quant* q, int mode) {
 
 sattn_status hip_status(hipError_t e) { return e == hipSuccess ? SATTN_OK : SATTN_ERR_HIP; }
 
+// The quantization pass; with_q = false skips the Q blocks (the attention kernel of the drop-in calls quantizes them).
 sattn_status do_quantize(const sattn_tensor* q, const sattn_tensor* k, const sattn_tensor* v, int mode,
-                         const sattn_quant* out, void* scratch, size_t scratch_bytes_, hipStream_t s) {
+                         const sattn_quant* out, void* scratch, size_t scratch_bytes_, hipStream_t s,
+                         bool with_q = true) {
   const QuantArg qa = quant_arg(*out);
   const TensorArg kt = tensor_arg(k), vt = tensor_arg(v);
   hipError_t e = hipSuccess;
@@ -138,7 +142,7 @@ sattn_status do_quantize(const sattn_tensor* q, const sattn_tensor* k, const sat
     float* vinv = mode == SATTN_MODE_I8_FP8 ? reinterpret_cast<float*>(static_cast<char*>(scratch) + 2 * runs) : nullptr;
     (void)scratch_bytes_;
     const bool with_v = mode == SATTN_MODE_I8_FP8;
-    if ((e = launch_quant_q(tensor_arg(q), qa, s)) != hipSuccess) return hip_status(e);
+    if (with_q && (e = launch_quant_q(tensor_arg(q), qa, s)) != hipSuccess) return hip_status(e);
     if ((e = launch_kv_stats(kt, vt, with_v, qa, ksum, vmax, s)) != hipSuccess) return hip_status(e);
     if ((e = launch_kv_finalize(qa, with_v, ksum, vmax, vinv, s)) != hipSuccess) return hip_status(e);
     e = launch_kv_quant(kt, vt, mode, qa, vinv, s);
@@ -148,8 +152,9 @@ sattn_status do_quantize(const sattn_tensor* q, const sattn_tensor* k, const sat
   return hip_status(e);
 }
 
-sattn_status layout(int B, int H, int Nq, int Nkv, int d, int blk_q, int blk_k, int mode, void* base, sattn_quant* out) {
-  const Sizes z = sizes(B, H, Nq, Nkv, d, blk_q, mode);
+sattn_status layout(int B, int H, int Nq, int Nkv, int d, int blk_q, int blk_k, int mode, void* base, sattn_quant* out,
+                    bool with_q = true) {
+  const Sizes z = sizes(B, H, Nq, Nkv, d, blk_q, mode, with_q);
   std::memset(out, 0, sizeof(*out));
   out->B = B;
   out->H = H;
@@ -191,21 +196,23 @@ sattn_status fwd_common(const sattn_tensor* q, const sattn_tensor* k, const satt
   if ((st = check_shape(B, H, Nq, Nkv, d, blk_q, blk_k, mode)) != SATTN_OK) return st;
   if ((st = check_k_rows(k, mode)) != SATTN_OK) return st;
   if (!(std::isfinite(sm_scale))) return SATTN_ERR_INVALID_ARG;
-  const Sizes z = sizes(B, H, Nq, Nkv, d, blk_q, mode);
+  // Q is quantized inside the attention kernel (modes 1 and 2): the workspace holds K, V and the partial sums only
+  const Sizes z = sizes(B, H, Nq, Nkv, d, blk_q, mode, false);
   const size_t need = z.total + scratch_bytes(B, H, Nkv, d, mode);
   if (!ws || ws_bytes < need) return SATTN_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(ws) % kAlign) != 0) return SATTN_ERR_INVALID_ARG;
   sattn_quant qk;
-  layout(B, H, Nq, Nkv, d, blk_q, blk_k, mode, ws, &qk);
+  layout(B, H, Nq, Nkv, d, blk_q, blk_k, mode, ws, &qk, false);
   void* scratch = static_cast<char*>(ws) + z.total;
+  const bool fuse_q = mode != SATTN_MODE_BF16;
   clear_pending_error();
-  if ((st = hip_status(prepare_attn(mode, d, mask != nullptr))) != SATTN_OK) return st;
-  st = do_quantize(q, k, v, mode, &qk, scratch, need - z.total, s);
+  if ((st = hip_status(prepare_attn(mode, d, mask != nullptr, fuse_q))) != SATTN_OK) return st;
+  st = do_quantize(q, k, v, mode, &qk, scratch, need - z.total, s, false);
   if (st != SATTN_OK) return st;
   const float c = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt((float)d);
   const TensorArg ot = tensor_arg(o);
   return hip_status(launch_attn(mode, tensor_arg(q), tensor_arg(k), quant_arg(qk), const_cast<uint16_t*>(ot.ptr), ot.sb,
-                                ot.sh, ot.sn, c, mask, s));
+                                ot.sh, ot.sn, c, mask, fuse_q, s));
 }
 
 }  // namespace
@@ -250,7 +257,7 @@ size_t sattn_quantize_scratch_bytes(int B, int H, int Nkv, int d, int mode) {
 
 size_t sattn_workspace_bytes(int B, int H, int Nq, int Nkv, int d, int blk_q, int blk_k, int mode) {
   if (check_shape(B, H, Nq, Nkv, d, blk_q, blk_k, mode) != SATTN_OK) return 0;
-  return sizes(B, H, Nq, Nkv, d, blk_q, mode).total + scratch_bytes(B, H, Nkv, d, mode);
+  return sizes(B, H, Nq, Nkv, d, blk_q, mode, false).total + scratch_bytes(B, H, Nkv, d, mode);
 }
 
 sattn_status sattn_quantize(const sattn_tensor* q, const sattn_tensor* k, const sattn_tensor* v, int mode,
@@ -284,9 +291,9 @@ sattn_status sattn_fwd_quantized(const sattn_tensor* q, const sattn_tensor* k, c
   const TensorArg qt = mode == SATTN_MODE_BF16 ? tensor_arg(q) : none;
   const TensorArg kt = mode == SATTN_MODE_BF16 ? tensor_arg(k) : none;
   clear_pending_error();
-  if ((st = hip_status(prepare_attn(mode, qk->d, false))) != SATTN_OK) return st;
+  if ((st = hip_status(prepare_attn(mode, qk->d, false, false))) != SATTN_OK) return st;
   return hip_status(launch_attn(mode, qt, kt, quant_arg(*qk), const_cast<uint16_t*>(ot.ptr), ot.sb, ot.sh, ot.sn, c,
-                                nullptr, reinterpret_cast<hipStream_t>(stream)));
+                                nullptr, false, reinterpret_cast<hipStream_t>(stream)));
 }
 
 sattn_status sattn_fwd(const sattn_tensor* q, const sattn_tensor* k, const sattn_tensor* v, const sattn_tensor* o,

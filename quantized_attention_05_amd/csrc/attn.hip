@@ -20,6 +20,7 @@
 // "显存优化 / 量化"); the per-call mode is its layer-selective precision (section "保持视频质量").
 #include <type_traits>
 
+#include "quant_rules.h"
 #include "sattn_internal.h"
 
 namespace sattn {
@@ -187,11 +188,17 @@ struct PTile<2> {
   v8i w;
 };
 
-template <int MODE, int D, int W, bool SPARSE>
+// FUSEQ (modes 1 and 2): the kernel quantizes its own Q block from the bf16 Q tensor instead of reading the codes of
+// a separate pass.  The workgroup's 128 query rows are exactly one Q block when blk_q = 128 (two when it is 64), so the
+// block's amax is one workgroup reduction, and codes and scale follow the same rule as the quantization pass
+// (quant_rules.h): a = max|Q| over the block's valid rows, a < 2^-100 -> scale 0 and codes 0, else
+// scale = a/127 and code = clamp(rint(x * (127/a)), -127, 127).
+template <int MODE, int D, int W, bool SPARSE, bool FUSEQ>
 __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
   using G = Geo<MODE, D>;
   using RG = Ring<MODE, D, W>;
   static_assert(!SPARSE || W * kRowsPerWave == kMaskQRows, "one mask row per workgroup query tile");
+  static_assert(!FUSEQ || (MODE != 0 && W * kRowsPerWave == 128), "a workgroup quantizes one 128-row Q block");
   using SAcc = std::conditional_t<MODE == 0, v16f, v16i>;  // scores: fp32 (bf16 op) or biased int32 (INT8 op)
   constexpr int CB = G::CB;
   constexpr int KS = G::KSTEPS;
@@ -277,7 +284,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
       else qfb[s] = (v8bf){};
     }
     fq = a.clog2e;
-  } else {
+  } else if constexpr (!FUSEQ) {
     if (active) {
       const int8_t* src = a.qa.q_codes + (bh * a.qa.nqb * a.qa.blk_q + q0 + n) * D;
 #pragma unroll
@@ -287,6 +294,35 @@ __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) qf8[s] = (v4i){};
     }
+  }
+  // FUSEQ: this lane's bf16 Q values (row q0 + n, channels 32 s + 16 g ..), kept raw until the block's amax is known
+  // (after the prologue's barrier); the wave's part of the amax goes to LDS now
+  __shared__ float qred[FUSEQ ? W : 1];
+  uint4 qraw[FUSEQ ? 2 * KS : 1];
+  if constexpr (FUSEQ) {
+    const int row = q0 + n;
+    float am = 0.0f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      if (row < a.qa.Nq) {
+        const uint16_t* src = a.q.ptr + b * a.q.sb + h * a.q.sh + (int64_t)row * a.q.sn + 32 * s + 16 * g;
+        qraw[2 * s] = *reinterpret_cast<const uint4*>(src);
+        qraw[2 * s + 1] = *reinterpret_cast<const uint4*>(src + 8);
+      } else {
+        qraw[2 * s] = make_uint4(0, 0, 0, 0);
+        qraw[2 * s + 1] = make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float f[8];
+        unpack8(qraw[2 * s + j], f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(f[i]));
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
+    if (lane == 0) qred[wave] = am;  // read after the prologue's __syncthreads
   }
   const float* kscale = (MODE == 0) ? nullptr : a.qa.k_scales + bh * nkb;
 
@@ -520,6 +556,40 @@ __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
   SAcc sa[2], sb[2];
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  if constexpr (FUSEQ) {
+    // the block's amax: all W waves (blk_q = 128) or this wave's pair (blk_q = 64, two blocks per workgroup)
+    float am;
+    if (a.qa.blk_q == 128) {
+      am = qred[0];
+#pragma unroll
+      for (int w = 1; w < W; ++w) am = fmaxf(am, qred[w]);
+    } else {
+      am = fmaxf(qred[wave & ~1], qred[wave | 1]);
+    }
+    const bool zero = !(am >= kGuard);
+    const float inv = zero ? 0.0f : 127.0f / am;
+    fq = (zero ? 0.0f : am / 127.0f) * a.clog2e;
+    const bool row_ok = !zero && q0 + n < a.qa.Nq;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      int wv[4];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float f[8];
+        unpack8(qraw[2 * s + j], f);
+        uint32_t lo = 0, hi = 0;
+        if (row_ok) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lo |= (uint32_t)(uint8_t)code_i8(f[i], inv) << (8 * i);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) hi |= (uint32_t)(uint8_t)code_i8(f[4 + i], inv) << (8 * i);
+        }
+        wv[2 * j] = (int)lo;
+        wv[2 * j + 1] = (int)hi;
+      }
+      qf8[s] = (v4i){wv[0], wv[1], wv[2], wv[3]};
+    }
+  }
   ks = (MODE == 0) ? 1.0f : *reinterpret_cast<const float*>(slots + DIST * RG::SLOT);
   qk(smem + DIST * G::STAGE, sa);
 
@@ -615,36 +685,51 @@ __global__ void __launch_bounds__(64) debug_qk_kernel(QuantArg qa, int64_t bh, i
   }
 }
 
+// The kernel instance of a call: dense or block-sparse, Q codes read or quantized in the kernel (modes 1 and 2).
 template <int MODE, int D>
-hipError_t launch_attn_t(AttnArg a, hipStream_t s) {
+const void* attn_kernel_for(bool sparse, bool fuse_q) {
+  constexpr int W = pipe_waves<MODE, D>();
+  if constexpr (MODE == 0) {
+    return sparse ? reinterpret_cast<const void*>(&attn_pipe_kernel<MODE, D, W, true, false>)
+                  : reinterpret_cast<const void*>(&attn_pipe_kernel<MODE, D, W, false, false>);
+  } else {
+    if (sparse)
+      return fuse_q ? reinterpret_cast<const void*>(&attn_pipe_kernel<MODE, D, W, true, true>)
+                    : reinterpret_cast<const void*>(&attn_pipe_kernel<MODE, D, W, true, false>);
+    return fuse_q ? reinterpret_cast<const void*>(&attn_pipe_kernel<MODE, D, W, false, true>)
+                  : reinterpret_cast<const void*>(&attn_pipe_kernel<MODE, D, W, false, false>);
+  }
+}
+
+template <int MODE, int D>
+hipError_t launch_attn_t(AttnArg a, bool fuse_q, hipStream_t s) {
   constexpr int W = pipe_waves<MODE, D>();
   using RG = Ring<MODE, D, W>;
   const bool sparse = a.mask != nullptr;
-  const auto kernel = sparse ? &attn_pipe_kernel<MODE, D, W, true> : &attn_pipe_kernel<MODE, D, W, false>;
   // dense: the ring; block-sparse: the ring + the tile list (sized for this call's key tiles)
   const int bytes = sparse ? RG::LIST_OFF + 16 + cdiv(2 * a.qa.nkb, 16) * 16 : RG::BYTES;
   a.nqt = cdiv(a.qa.Nq, W * kRowsPerWave);
   const int64_t nwg = (int64_t)a.nqt * a.qa.H * a.qa.B;  // below 2^31 by the host's shape checks
-  kernel<<<(int)nwg, 64 * W, bytes, s>>>(a);
-  return hipGetLastError();
+  void* args[] = {&a};
+  const hipError_t e = hipLaunchKernel(attn_kernel_for<MODE, D>(sparse, fuse_q), dim3((unsigned)nwg), dim3(64 * W),
+                                       args, bytes, s);
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 // The dynamic LDS limit of the kernel a call will launch (more than the default 64 KiB in mode 2), set on the current
 // device before anything is enqueued.  Set on every call rather than remembered, so that no state is kept and a
 // second GPU of the process gets it too.
 template <int MODE, int D>
-hipError_t prepare_attn_t(bool sparse) {
-  constexpr int W = pipe_waves<MODE, D>();
-  using RG = Ring<MODE, D, W>;
-  const auto kernel = sparse ? &attn_pipe_kernel<MODE, D, W, true> : &attn_pipe_kernel<MODE, D, W, false>;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+hipError_t prepare_attn_t(bool sparse, bool fuse_q) {
+  using RG = Ring<MODE, D, pipe_waves<MODE, D>()>;
+  return hipFuncSetAttribute(attn_kernel_for<MODE, D>(sparse, fuse_q), hipFuncAttributeMaxDynamicSharedMemorySize,
                              sparse ? RG::SPARSE_BYTES : RG::BYTES);
 }
 
 }  // namespace
 
 hipError_t launch_attn(int mode, const TensorArg& q, const TensorArg& k, const QuantArg& qa, uint16_t* o, int64_t osb,
-                       int64_t osh, int64_t osn, float sm_scale, const uint8_t* mask, hipStream_t s) {
+                       int64_t osh, int64_t osn, float sm_scale, const uint8_t* mask, bool fuse_q, hipStream_t s) {
   AttnArg a;
   a.q = q;
   a.k = k;
@@ -656,24 +741,24 @@ hipError_t launch_attn(int mode, const TensorArg& q, const TensorArg& k, const Q
   a.clog2e = sm_scale * 1.4426950408889634f;
   a.mask = mask;
   if (qa.d == 128) {
-    if (mode == 0) return launch_attn_t<0, 128>(a, s);
-    if (mode == 1) return launch_attn_t<1, 128>(a, s);
-    return launch_attn_t<2, 128>(a, s);
+    if (mode == 0) return launch_attn_t<0, 128>(a, fuse_q, s);
+    if (mode == 1) return launch_attn_t<1, 128>(a, fuse_q, s);
+    return launch_attn_t<2, 128>(a, fuse_q, s);
   }
-  if (mode == 0) return launch_attn_t<0, 64>(a, s);
-  if (mode == 1) return launch_attn_t<1, 64>(a, s);
-  return launch_attn_t<2, 64>(a, s);
+  if (mode == 0) return launch_attn_t<0, 64>(a, fuse_q, s);
+  if (mode == 1) return launch_attn_t<1, 64>(a, fuse_q, s);
+  return launch_attn_t<2, 64>(a, fuse_q, s);
 }
 
-hipError_t prepare_attn(int mode, int d, bool sparse) {
+hipError_t prepare_attn(int mode, int d, bool sparse, bool fuse_q) {
   if (d == 128) {
-    if (mode == 0) return prepare_attn_t<0, 128>(sparse);
-    if (mode == 1) return prepare_attn_t<1, 128>(sparse);
-    return prepare_attn_t<2, 128>(sparse);
+    if (mode == 0) return prepare_attn_t<0, 128>(sparse, fuse_q);
+    if (mode == 1) return prepare_attn_t<1, 128>(sparse, fuse_q);
+    return prepare_attn_t<2, 128>(sparse, fuse_q);
   }
-  if (mode == 0) return prepare_attn_t<0, 64>(sparse);
-  if (mode == 1) return prepare_attn_t<1, 64>(sparse);
-  return prepare_attn_t<2, 64>(sparse);
+  if (mode == 0) return prepare_attn_t<0, 64>(sparse, fuse_q);
+  if (mode == 1) return prepare_attn_t<1, 64>(sparse, fuse_q);
+  return prepare_attn_t<2, 64>(sparse, fuse_q);
 }
 
 int attn_rows_per_workgroup() { return 4 * kRowsPerWave; }

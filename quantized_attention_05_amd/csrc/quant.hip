@@ -10,26 +10,11 @@
 //   V: per-channel a_c over all tokens; scale = a_c/448, code = E4M3(v * (448/a_c)), RNE, saturating.
 #pragma clang fp contract(off)
 
+#include "quant_rules.h"
 #include "sattn_internal.h"
 
 namespace sattn {
 namespace {
-
-__device__ __forceinline__ float bf2f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
-
-// 8 bf16 values (16 bytes) -> 8 floats
-__device__ __forceinline__ void unpack8(const uint4& u, float* f) {
-  f[0] = bf2f(u.x & 0xFFFFu); f[1] = bf2f(u.x >> 16);
-  f[2] = bf2f(u.y & 0xFFFFu); f[3] = bf2f(u.y >> 16);
-  f[4] = bf2f(u.z & 0xFFFFu); f[5] = bf2f(u.z >> 16);
-  f[6] = bf2f(u.w & 0xFFFFu); f[7] = bf2f(u.w >> 16);
-}
-
-__device__ __forceinline__ int8_t code_i8(float x, float inv) {
-  float q = rintf(x * inv);
-  q = fminf(fmaxf(q, -127.0f), 127.0f);
-  return (int8_t)(int)q;
-}
 
 // max over the 256 threads of a block (4 waves of 64)
 __device__ __forceinline__ float block_max256(float v, float* red) {

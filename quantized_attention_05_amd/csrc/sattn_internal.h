@@ -40,7 +40,7 @@ struct QuantArg {
 };
 
 // Per-call set-up of the attention kernel a call will launch (its dynamic LDS limit); enqueues nothing.
-hipError_t prepare_attn(int mode, int d, bool sparse);
+hipError_t prepare_attn(int mode, int d, bool sparse, bool fuse_q);
 // Query rows of one attention workgroup (the grid has ceil(Nq / rows) * H * B workgroups).
 int attn_rows_per_workgroup();
 
@@ -52,9 +52,10 @@ hipError_t launch_kv_finalize(const QuantArg& qa, bool with_v, const float* ksum
                               hipStream_t s);
 hipError_t launch_kv_quant(const TensorArg& k, const TensorArg& v, int mode, const QuantArg& qa, const float* vinv,
                            hipStream_t s);
-// mask: nullptr for dense attention, else the block-sparse mask [B, H, ceil(Nq/128), ceil(Nkv/64)] (device bytes)
+// mask: nullptr for dense attention, else the block-sparse mask [B, H, ceil(Nq/128), ceil(Nkv/64)] (device bytes).
+// fuse_q (modes 1 and 2): quantize Q from the bf16 tensor q inside the kernel instead of reading qa's Q codes.
 hipError_t launch_attn(int mode, const TensorArg& q, const TensorArg& k, const QuantArg& qa, uint16_t* o, int64_t osb,
-                       int64_t osh, int64_t osn, float sm_scale, const uint8_t* mask, hipStream_t s);
+                       int64_t osh, int64_t osn, float sm_scale, const uint8_t* mask, bool fuse_q, hipStream_t s);
 hipError_t launch_error_stats(const TensorArg& a, const TensorArg& r, int B, int H, int N, int d, double* out,
                               hipStream_t s);
 hipError_t launch_debug_qk(const QuantArg& qa, int b, int h, int q0, int nq, int k0, int nk, int32_t* out,

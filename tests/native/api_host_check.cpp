@@ -49,7 +49,7 @@ hipError_t launch_kv_quant(const TensorArg&, const TensorArg&, int, const QuantA
   return record("kv_quant");
 }
 hipError_t launch_attn(int, const TensorArg&, const TensorArg&, const QuantArg&, uint16_t*, int64_t, int64_t, int64_t,
-                       float, const uint8_t*, hipStream_t) {
+                       float, const uint8_t*, bool, hipStream_t) {
   return record("attn");
 }
 hipError_t launch_error_stats(const TensorArg&, const TensorArg&, int, int, int, int, double*, hipStream_t) {
@@ -58,7 +58,7 @@ hipError_t launch_error_stats(const TensorArg&, const TensorArg&, int, int, int,
 hipError_t launch_debug_qk(const QuantArg&, int, int, int, int, int, int, int32_t*, hipStream_t) {
   return record("debug_qk");
 }
-hipError_t prepare_attn(int, int, bool) { return record("prepare_attn"); }
+hipError_t prepare_attn(int, int, bool, bool) { return record("prepare_attn"); }
 int attn_rows_per_workgroup() { return 128; }
 hipError_t launch_quant_blocks(const uint16_t*, int, int, int64_t, int8_t*, float*, hipStream_t) {
   return record("quant_blocks");
@@ -94,9 +94,12 @@ void check_sizes() {
         const int B = sh[0], H = sh[1], Nq = sh[2], Nkv = sh[3], d = sh[4];
         const size_t qb = sattn_quant_bytes(B, H, Nq, Nkv, d, blk_q, 64, mode);
         const size_t wb = sattn_workspace_bytes(B, H, Nq, Nkv, d, blk_q, 64, mode);
-        EXPECT(qb > 0 && wb >= qb);
+        EXPECT(qb > 0 && wb > 0);
+        EXPECT(mode != 0 || wb >= qb);
         const size_t codes = (size_t)B * H * d * ((size_t)(Nq + blk_q - 1) / blk_q * blk_q);
         EXPECT(mode == 0 || qb >= codes);
+        // the drop-in workspace leaves out the Q codes (quantized inside the attention kernel)
+        EXPECT(mode == 0 || wb + codes <= qb + sattn_quantize_scratch_bytes(B, H, Nkv, d, mode) + 512);
         EXPECT(sattn_workspace_bytes(B, H, Nq + 1, Nkv, d, blk_q, 64, mode) >= wb || Nq == (1 << 28));
         sattn_quant q;
         const uintptr_t base = uintptr_t{1} << 44;
@@ -134,8 +137,8 @@ void check_fwd() {
     const int reads = g_last_error_reads;
     EXPECT(call(&q, ws, reinterpret_cast<void*>(kFake)) == SATTN_OK);
     EXPECT(g_last_error_reads > reads);  // a pending error is cleared before the first launch
-    const std::string want = mode == 0 ? "prepare_attn,kv_quant,attn"
-                                       : "prepare_attn,quant_q,kv_stats,kv_finalize,kv_quant,attn";
+    // the drop-in call quantizes Q inside the attention kernel: no separate Q pass
+    const std::string want = mode == 0 ? "prepare_attn,kv_quant,attn" : "prepare_attn,kv_stats,kv_finalize,kv_quant,attn";
     EXPECT(joined() == want);
     // host-side errors enqueue nothing
     EXPECT(call(&q, ws - 1, reinterpret_cast<void*>(kFake)) == SATTN_ERR_WORKSPACE && g_log.empty());
