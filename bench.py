@@ -332,6 +332,8 @@ def main():
                     help="a name from quantized_attention_05_amd.workloads.WORKLOADS, 'layersel', 'sparse', 'probe' or "
                          "'linear'")
     ap.add_argument("--mode", type=int, default=2, choices=[0, 1, 2])
+    ap.add_argument("--nkv", type=int, default=None,
+                    help="key sequence length instead of the workload's own (same recipe; e.g. a cross-attention sweep)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=None, help="attention-kernel-only timing reps")
@@ -373,6 +375,8 @@ def main():
     from quantized_attention_05_amd import workloads as wl
 
     w = wl.WORKLOADS[args.workload]
+    if args.nkv is not None and args.nkv != w.Nkv:
+        w = wl.scaled(w, name=f"{w.name}-nkv{args.nkv}", Nkv=args.nkv)
     mode = args.mode
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -295,34 +295,23 @@ __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
       for (int s = 0; s < KS; ++s) qf8[s] = (v4i){};
     }
   }
-  // FUSEQ: this lane's bf16 Q values (row q0 + n, channels 32 s + 16 g ..), kept raw until the block's amax is known
-  // (after the prologue's barrier); the wave's part of the amax goes to LDS now
+  // FUSEQ: this lane's bf16 Q values (row q0 + n, channels 32 s + 16 g ..), loaded now and used once the prologue's
+  // tile loads are in flight too (their latencies overlap): the amax goes through LDS, the codes follow the barrier
   __shared__ float qred[FUSEQ ? W : 1];
   uint4 qraw[FUSEQ ? 2 * KS : 1];
   if constexpr (FUSEQ) {
     const int row = q0 + n;
-    float am = 0.0f;
+    if (row < a.qa.Nq) {
+      const uint16_t* src = a.q.ptr + b * a.q.sb + h * a.q.sh + (int64_t)row * a.q.sn + 16 * g;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      if (row < a.qa.Nq) {
-        const uint16_t* src = a.q.ptr + b * a.q.sb + h * a.q.sh + (int64_t)row * a.q.sn + 32 * s + 16 * g;
-        qraw[2 * s] = *reinterpret_cast<const uint4*>(src);
-        qraw[2 * s + 1] = *reinterpret_cast<const uint4*>(src + 8);
-      } else {
-        qraw[2 * s] = make_uint4(0, 0, 0, 0);
-        qraw[2 * s + 1] = make_uint4(0, 0, 0, 0);
+      for (int s = 0; s < KS; ++s) {
+        qraw[2 * s] = *reinterpret_cast<const uint4*>(src + 32 * s);
+        qraw[2 * s + 1] = *reinterpret_cast<const uint4*>(src + 32 * s + 8);
       }
+    } else {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        float f[8];
-        unpack8(qraw[2 * s + j], f);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(f[i]));
-      }
+      for (int j = 0; j < 2 * KS; ++j) qraw[j] = make_uint4(0, 0, 0, 0);
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
-    if (lane == 0) qred[wave] = am;  // read after the prologue's __syncthreads
   }
   const float* kscale = (MODE == 0) ? nullptr : a.qa.k_scales + bh * nkb;
 
@@ -532,7 +521,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
     if constexpr (MODE == 2) asm volatile("" ::"v"(pcur.w), "v"(l));
     else asm volatile("" ::"v"(pcur.b[0]), "v"(pcur.b[1]), "v"(pcur.b[2]), "v"(pcur.b[3]), "v"(l));
 #endif
-    if (__any(m != mold)) {
+    if (i > 0 && __any(m != mold)) {  // (on the first tile the accumulator is still zero)
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -554,6 +543,19 @@ __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
     *reinterpret_cast<uint4*>(smem + G::KBYTES + 16 * i) = make_uint4(0, 0, 0, 0);
   PTile<MODE> pa = {}, pb = {};
   SAcc sa[2], sb[2];
+  if constexpr (FUSEQ) {  // the wave's part of the Q block's amax
+    float am = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 2 * KS; ++j) {
+      float f[8];
+      unpack8(qraw[j], f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(f[i]));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
+    if (lane == 0) qred[wave] = am;  // read after the barrier below
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if constexpr (FUSEQ) {
