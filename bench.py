@@ -476,7 +476,7 @@ def main():
             "frac": round(achieved / PEAK_TOPS[mode], 4),
             "traffic": traffic_detail["total_bytes"] if traffic_detail else None,
             "traffic_detail": traffic_detail,
-            "kernel": f"attn_pipe_kernel<{mode}, {w.d}, 4>",
+            "kernel": f"attn_pipe_kernel<{mode}, {w.d}, 4, false, false>",
             "ops_per_launch": w.ops,
         },
         "wall_s_timed_region": round(wall, 3),
