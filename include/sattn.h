@@ -198,9 +198,14 @@ sattn_status sattn_fwd_block_sparse(const sattn_tensor* q, const sattn_tensor* k
  * same inputs), writes per (b, h) the fp64 sums over rows and channels
  *   out[(b*H + h)*4 + 0..3] = sum (a - ref)^2, sum ref^2, sum a*ref, sum a^2
  * (relative L2 error = sqrt(out0 / out1), cosine = out2 / sqrt(out1 * out3)).  out: device memory, 8-byte aligned,
- * B*H*4 doubles.  Deterministic (fixed summation order); allocates nothing.  Errors: SATTN_ERR_INVALID_ARG for
- * NULL or mismatched tensors, SATTN_ERR_UNSUPPORTED for d outside {64, 128} or B*H > 65535. */
-sattn_status sattn_error_stats(const sattn_tensor* a, const sattn_tensor* ref, double* out, sattn_stream_t stream);
+ * B*H*4 doubles.  ws: device memory, 8-byte aligned, at least sattn_error_stats_workspace_bytes(B, H, N) bytes, for
+ * the per-chunk partial sums (each head's rows are summed in up to 64 chunks, then the chunks are added).
+ * Deterministic: the summation order depends on the shape alone.  Errors: SATTN_ERR_INVALID_ARG for NULL or
+ * mismatched tensors or a misaligned out or ws, SATTN_ERR_UNSUPPORTED for d outside {64, 128} or B*H > 65535,
+ * SATTN_ERR_WORKSPACE for a NULL or too small ws. */
+size_t sattn_error_stats_workspace_bytes(int B, int H, int N); /* 0 for an empty shape */
+sattn_status sattn_error_stats(const sattn_tensor* a, const sattn_tensor* ref, double* out, void* ws, size_t ws_bytes,
+                               sattn_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------------------------------
  * Quantized linear layer (TMAP I2V write-up, section "FFN性能优化", subsection "线性层量化"): the weights of the

@@ -318,7 +318,13 @@ sattn_status sattn_cross_fwd(const sattn_tensor* q, const sattn_tensor* k, const
   return fwd_common(q, k, v, o, sm_scale, mode, 128, kTile, ws, ws_bytes, nullptr, reinterpret_cast<hipStream_t>(stream));
 }
 
-sattn_status sattn_error_stats(const sattn_tensor* a, const sattn_tensor* ref, double* out, sattn_stream_t stream) {
+size_t sattn_error_stats_workspace_bytes(int B, int H, int N) {
+  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  return align_up((size_t)B * H * error_stats_chunks(N) * 4 * sizeof(double));
+}
+
+sattn_status sattn_error_stats(const sattn_tensor* a, const sattn_tensor* ref, double* out, void* ws, size_t ws_bytes,
+                               sattn_stream_t stream) {
   if (!a || !ref || !out) return SATTN_ERR_INVALID_ARG;
   if (a->B <= 0 || a->H <= 0 || a->N <= 0) return SATTN_ERR_INVALID_ARG;
   sattn_status st;
@@ -326,9 +332,11 @@ sattn_status sattn_error_stats(const sattn_tensor* a, const sattn_tensor* ref, d
   if ((st = check_tensor(ref, a->B, a->H, a->N, a->d)) != SATTN_OK) return st;
   if (reinterpret_cast<uintptr_t>(out) % 8 != 0) return SATTN_ERR_INVALID_ARG;
   if ((a->d != 64 && a->d != 128) || (int64_t)a->B * a->H > 65535) return SATTN_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < sattn_error_stats_workspace_bytes(a->B, a->H, a->N)) return SATTN_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % 8 != 0) return SATTN_ERR_INVALID_ARG;
   clear_pending_error();
-  return hip_status(launch_error_stats(tensor_arg(a), tensor_arg(ref), a->B, a->H, a->N, a->d, out,
-                                       reinterpret_cast<hipStream_t>(stream)));
+  return hip_status(launch_error_stats(tensor_arg(a), tensor_arg(ref), a->B, a->H, a->N, a->d,
+                                       static_cast<double*>(ws), out, reinterpret_cast<hipStream_t>(stream)));
 }
 
 sattn_status sattn_debug_qk_int32(const sattn_quant* qk, int b, int h, int q0, int nq, int k0, int nk, int32_t* out,

@@ -70,7 +70,8 @@ SYMBOLS = [
     ("sattn_fwd_noalloc", _I, [_TP, _TP, _TP, _TP, ctypes.c_float, _I, _I, _I, _P]),
     ("sattn_cross_fwd", _I, [_TP, _TP, _TP, _TP, ctypes.c_float, _I, _P, _SZ, _P]),
     ("sattn_fwd_block_sparse", _I, [_TP, _TP, _TP, _TP, _P, ctypes.c_float, _I, _I, _I, _P, _SZ, _P]),
-    ("sattn_error_stats", _I, [_TP, _TP, _P, _P]),
+    ("sattn_error_stats_workspace_bytes", _SZ, [_I, _I, _I]),
+    ("sattn_error_stats", _I, [_TP, _TP, _P, _P, _SZ, _P]),
     ("sattn_debug_qk_int32", _I, [_QP, _I, _I, _I, _I, _I, _I, _P, _P]),
     ("sattn_quantize_blocks", _I, [_P, _I, _I, ctypes.c_int64, _P, _P, _P]),
     ("sattn_linear_workspace_bytes", _SZ, [_I, _I, _I, _I]),
@@ -157,9 +158,13 @@ def sattn_fwd_block_sparse(q, k, v, o, block_mask: int, sm_scale, mode, blk_q, b
                                         ctypes.c_void_p(stream)), "sattn_fwd_block_sparse")
 
 
-def sattn_error_stats(a, ref, out: int, stream: int):
-    _check(lib().sattn_error_stats(_ref(a), _ref(ref), ctypes.c_void_p(out), ctypes.c_void_p(stream)),
-           "sattn_error_stats")
+def sattn_error_stats_workspace_bytes(B, H, N) -> int:
+    return lib().sattn_error_stats_workspace_bytes(B, H, N)
+
+
+def sattn_error_stats(a, ref, out: int, ws: int, ws_bytes: int, stream: int):
+    _check(lib().sattn_error_stats(_ref(a), _ref(ref), ctypes.c_void_p(out), ctypes.c_void_p(ws), ws_bytes,
+                                   ctypes.c_void_p(stream)), "sattn_error_stats")
 
 
 def sattn_debug_qk_int32(qk: sattn_quant, b, h, q0, nq, k0, nk, out: int, stream: int):
@@ -290,13 +295,14 @@ def cross_fwd(q, k, v, mode=SATTN_MODE_BF16, sm_scale=None, out=None, workspace=
     return o
 
 
-def error_stats(a, ref):
+def error_stats(a, ref, workspace=None):
     """Per-head fp64 sums [sum (a-ref)^2, sum ref^2, sum a*ref, sum a^2] of two [B, H, N, d] bf16 GPU tensors
     through sattn_error_stats.  Returns a [B, H, 4] float64 GPU tensor."""
     dev = _same_device("error_stats", a, ref)
-    B, H = a.shape[0], a.shape[1]
+    B, H, N = a.shape[0], a.shape[1], a.shape[2]
+    ws = _workspace("error_stats", workspace, sattn_error_stats_workspace_bytes(B, H, N), dev)
     out = torch.empty((B, H, 4), dtype=torch.float64, device=dev)
-    sattn_error_stats(tensor_desc(a), tensor_desc(ref), out.data_ptr(), _stream())
+    sattn_error_stats(tensor_desc(a), tensor_desc(ref), out.data_ptr(), ws.data_ptr(), ws.numel(), _stream())
     return out
 
 

@@ -52,7 +52,7 @@ hipError_t launch_attn(int, const TensorArg&, const TensorArg&, const QuantArg&,
                        float, const uint8_t*, bool, hipStream_t) {
   return record("attn");
 }
-hipError_t launch_error_stats(const TensorArg&, const TensorArg&, int, int, int, int, double*, hipStream_t) {
+hipError_t launch_error_stats(const TensorArg&, const TensorArg&, int, int, int, int, double*, double*, hipStream_t) {
   return record("error_stats");
 }
 hipError_t launch_debug_qk(const QuantArg&, int, int, int, int, int, int, int32_t*, hipStream_t) {
@@ -172,7 +172,12 @@ void check_fwd() {
   EXPECT(sattn_fwd_block_sparse(&o, &o, &o, &o, nullptr, 0.0f, 2, 64, 64, reinterpret_cast<void*>(kFake), ws,
                                 nullptr) == SATTN_ERR_INVALID_ARG && g_log.empty());
   g_log.clear();
-  EXPECT(sattn_error_stats(&o, &o, reinterpret_cast<double*>(kFake), nullptr) == SATTN_OK && joined() == "error_stats");
+  const size_t ws_es = sattn_error_stats_workspace_bytes(1, 2, 256);
+  EXPECT(sattn_error_stats(&o, &o, reinterpret_cast<double*>(kFake), reinterpret_cast<void*>(kFake), ws_es, nullptr) ==
+         SATTN_OK && joined() == "error_stats");
+  g_log.clear();
+  EXPECT(sattn_error_stats(&o, &o, reinterpret_cast<double*>(kFake), reinterpret_cast<void*>(kFake), ws_es - 1,
+                           nullptr) == SATTN_ERR_WORKSPACE && g_log.empty());
   g_log.clear();
   EXPECT(sattn_debug_qk_int32(&qd, 0, 1, 0, 256, 0, 256, reinterpret_cast<int32_t*>(kFake), nullptr) == SATTN_OK);
   EXPECT(sattn_debug_qk_int32(&qd, 0, 2, 0, 4, 0, 4, reinterpret_cast<int32_t*>(kFake), nullptr) ==

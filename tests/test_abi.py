@@ -151,16 +151,25 @@ def test_argument_errors_are_caught_on_the_host(S):
     assert sparse(k=k_long) == S.SATTN_ERR_UNSUPPORTED
     assert sparse(ws=P + 16) == S.SATTN_ERR_INVALID_ARG            # reaches the workspace check
     assert sparse(k=_t(S, P, 1, 2, 200, 64), ws=P + 16) == S.SATTN_ERR_INVALID_ARG  # K rows != V rows
-    # error stats: both outputs of one shape, an 8-byte aligned output, d in {64, 128}, at most 65535 heads
-    es = L.sattn_error_stats
-    assert es(None, byref(o), ctypes.c_void_p(P), None) == S.SATTN_ERR_INVALID_ARG
-    assert es(byref(o), byref(o), None, None) == S.SATTN_ERR_INVALID_ARG
-    assert es(byref(o), byref(_t(S, P, 1, 2, 255, 64)), ctypes.c_void_p(P), None) == S.SATTN_ERR_INVALID_ARG
-    assert es(byref(o), byref(o), ctypes.c_void_p(P + 4), None) == S.SATTN_ERR_INVALID_ARG
+    # error stats: both outputs of one shape, 8-byte aligned out and ws, d in {64, 128}, at most 65535 heads,
+    # a large enough workspace
+    es, esw = L.sattn_error_stats, L.sattn_error_stats_workspace_bytes
+    ws_es = esw(1, 2, 256)
+    assert ws_es == 256 and esw(40, 1, 75600) == 40 * 64 * 32 and esw(0, 2, 256) == 0 and esw(1, 2, 0) == 0
+    def stats(a=o, r=o, out=P, ws=P, nws=ws_es):
+        return es(byref(a) if a else None, byref(r) if r else None, ctypes.c_void_p(out), ctypes.c_void_p(ws), nws,
+                  None)
+    assert stats(a=None) == S.SATTN_ERR_INVALID_ARG
+    assert stats(out=None) == S.SATTN_ERR_INVALID_ARG
+    assert stats(r=_t(S, P, 1, 2, 255, 64)) == S.SATTN_ERR_INVALID_ARG
+    assert stats(out=P + 4) == S.SATTN_ERR_INVALID_ARG
     o96 = _t(S, P, 1, 2, 256, 96)
-    assert es(byref(o96), byref(o96), ctypes.c_void_p(P), None) == S.SATTN_ERR_UNSUPPORTED
+    assert stats(a=o96, r=o96) == S.SATTN_ERR_UNSUPPORTED
     many = _t(S, P, 1, 65536, 1, 64)
-    assert es(byref(many), byref(many), ctypes.c_void_p(P), None) == S.SATTN_ERR_UNSUPPORTED
+    assert stats(a=many, r=many) == S.SATTN_ERR_UNSUPPORTED
+    assert stats(ws=None) == S.SATTN_ERR_WORKSPACE
+    assert stats(nws=ws_es - 1) == S.SATTN_ERR_WORKSPACE
+    assert stats(ws=P + 4) == S.SATTN_ERR_INVALID_ARG
     # quantized linear layer: every call below stops at a host check (the pointers are fake)
     vp = ctypes.c_void_p
     qb = L.sattn_quantize_blocks

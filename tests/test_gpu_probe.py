@@ -15,9 +15,12 @@ from parity_helpers import device_inputs, head_bits, say, u16
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("d,layout", [(128, "bhnd"), (64, "bhnd"), (128, "bnhd")])
-def test_error_stats_match_the_definition(d, layout):
-    w = wl.scaled(wl.WORKLOADS["wan14b-720p"], name="probe-stats", H=3, Nq=300, Nkv=300, d=d, seed=61)
+@pytest.mark.parametrize("d,layout,n", [(128, "bhnd", 300), (64, "bhnd", 300), (128, "bnhd", 300),
+                                        (128, "bhnd", 16500), (64, "bnhd", 16500), (128, "bhnd", 255)])
+def test_error_stats_match_the_definition(d, layout, n):
+    """N = 300 sums each head in 2 row chunks, N = 16500 in 64 chunks of 258 rows with a ragged last one (246),
+    N = 255 in a single chunk shorter than the workgroup's stride."""
+    w = wl.scaled(wl.WORKLOADS["wan14b-720p"], name="probe-stats", H=3, Nq=n, Nkv=n, d=d, seed=61)
     q, k, v = device_inputs(w, layout=layout)
     stats = sattn.error_stats(q, k).cpu().numpy()  # any two bf16 tensors of one shape
     qh, kh = u16(q), u16(k)
@@ -26,6 +29,11 @@ def test_error_stats_match_the_definition(d, layout):
         assert np.allclose(stats[0, h], ref, rtol=1e-12, atol=0), (h, stats[0, h], ref)
     same = sattn.error_stats(q, q).cpu().numpy()
     assert np.all(same[..., 0] == 0) and np.all(same[..., 1] == same[..., 2]) and np.all(same[..., 2] == same[..., 3])
+    # deterministic, and independent of what the workspace held before the call
+    dirty = torch.full((sattn.sattn_error_stats_workspace_bytes(w.B, w.H, n) + 512,), 0x7F, dtype=torch.uint8,
+                       device=q.device)
+    again = sattn.error_stats(q, k, workspace=dirty).cpu().numpy()
+    assert np.array_equal(again.view(np.uint64), stats.view(np.uint64))
 
 
 def oracle_layer_error(w, iteration):
