@@ -24,7 +24,7 @@ INT8_PEAK_TOPS = 5000.0
 HBM_PEAK_GBPS = 8000.0
 MODE_DTYPE = {0: "bf16", 1: "int8+bf16", 2: "int8+fp8e4m3"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "quantized_attention_05_amd", "csrc", f) for f in ("attn.hip", "sattn_internal.h")]
+KERNEL_SOURCES = [os.path.join(ROOT, "quantized_attention_05_amd", "csrc", f) for f in ("attn.hip", "sattn_internal.h", "quant_rules.h")]
 
 
 def kernel_source_hash() -> str:
@@ -48,6 +48,61 @@ def measured_traffic(workload: str, mode: int, launches_ops: float):
         return None
     return {"fetch_bytes": rec["fetch_bytes"], "write_bytes": rec["write_bytes"],
             "total_bytes": rec["fetch_bytes"] + rec["write_bytes"], "source": rec.get("source", TRAFFIC_FILE)}
+
+
+def record_traffic(root: str, workload: str, mode: int):
+    """Writes the measured HBM traffic of the timed attention kernel into the traffic table, from four rocprofv3 runs
+    under root (csv output, file prefix "run"): pmc_FETCH_SIZE and pmc_WRITE_SIZE of this benchmark (--steps 1
+    --warmup 0 --kernel-reps 1, so the timed instance runs as the kernel-alone reps) and copy_FETCH_SIZE and
+    copy_WRITE_SIZE of --calibrate-copy.  A counter's values are summed per dispatch over its instances; the copy of
+    a known byte count turns counter units into bytes.  Needs no GPU."""
+    import csv
+
+    from quantized_attention_05_amd import workloads as wl
+
+    def per_dispatch(run: str, match: str):
+        sums = {}
+        with open(os.path.join(root, run, "run_counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                if match in r["Kernel_Name"]:
+                    k = int(r["Dispatch_Id"])
+                    sums[k] = sums.get(k, 0.0) + float(r["Counter_Value"])
+        return [sums[k] for k in sorted(sums)]
+
+    kernel = f"attn_pipe_kernel<{mode}, 128, 4, false, false>"
+    copy_bytes = 1 << 28
+    fetch, write = per_dispatch("pmc_FETCH_SIZE", kernel), per_dispatch("pmc_WRITE_SIZE", kernel)
+    cf, cw = per_dispatch("copy_FETCH_SIZE", "copyBuffer"), per_dispatch("copy_WRITE_SIZE", "copyBuffer")
+    if not (fetch and write and cf and cw):
+        raise SystemExit(f"record-traffic: missing dispatches of {kernel} or of the copy under {root}")
+    ff = copy_bytes / 1024 / (sum(cf) / len(cf))  # counter unit -> KiB of traffic
+    fw = copy_bytes / 1024 / (sum(cw) / len(cw))
+    w = wl.WORKLOADS[workload]
+    nqb, nkb = -(-w.Nq // w.blk_q), -(-w.Nkv // 64)
+    # codes read once (Q, K, V: one byte per element), O written once (bf16), and the scales
+    algorithmic = w.B * w.H * (w.Nq * w.d + 2 * w.Nkv * w.d + 2 * w.Nq * w.d + 4 * (nqb + nkb + w.d))
+    try:
+        with open(TRAFFIC_FILE) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        table = {}
+    table[f"{workload}/mode{mode}"] = {
+        "kernel": kernel,
+        "kernel_source_sha": kernel_source_hash(),
+        "fetch_kib_per_dispatch": [round(x, 1) for x in fetch],
+        "write_kib_per_dispatch": [round(x, 1) for x in write],
+        "copy_calibration": {"bytes": copy_bytes, "fetch_kib": round(sum(cf) / len(cf), 1),
+                             "write_kib": round(sum(cw) / len(cw), 1), "fetch_factor": round(ff, 5),
+                             "write_factor": round(fw, 5)},
+        "fetch_bytes": round(sum(fetch) / len(fetch) * ff * 1024),
+        "write_bytes": round(sum(write) / len(write) * fw * 1024),
+        "algorithmic_bytes": algorithmic,
+        "source": "profiles/attn_kernel_wan14b-720p_i8fp8_traffic.md",
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(table, f, indent=1)
+        f.write("\n")
+    print(json.dumps(table[f"{workload}/mode{mode}"]))
 
 
 def layer_selective(args):
@@ -339,7 +394,14 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=None, help="attention-kernel-only timing reps")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run one plain 256 MiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--record-traffic", metavar="DIR", default=None,
+                    help="no GPU run: write the attention kernel's HBM traffic from the rocprofv3 counter runs under "
+                         "DIR into profiles/traffic.json")
     args = ap.parse_args()
+
+    if args.record_traffic:
+        record_traffic(args.record_traffic, args.workload, args.mode)
+        return
 
     if args.calibrate_copy:
         import torch

@@ -8,6 +8,7 @@
 #include <cstring>
 
 #include "linear_internal.h"
+#include "probe_internal.h"
 #include "sattn_internal.h"
 
 using namespace sattn;

@@ -9,7 +9,7 @@
 //   2. stats_final_kernel: one 64-lane workgroup per (batch, head) adds the G partials with a fixed tree.
 // The probe reads each output once (2 x 2 bytes per element) and is HBM-bound; G chunks per head spread a 40-head
 // 720p output over 2560 workgroups, where one workgroup per head would use 40 of the 256 compute units.
-#include "sattn_internal.h"
+#include "probe_internal.h"
 
 namespace sattn {
 namespace {

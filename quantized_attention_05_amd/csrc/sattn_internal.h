@@ -16,14 +16,6 @@ constexpr int kMaxSparseTiles = 32768;       // block-sparse: key tiles per mask
 
 inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
-// Row chunks per (batch, head) of the error-statistics reduction: one per 256 rows, at most 64.  A function of N
-// alone, so the summation order, and every bit of the result, depends on the shape only.
-constexpr int kStatsMaxChunks = 64;
-inline int error_stats_chunks(int N) {
-  const int g = cdiv(N, 256);
-  return g < kStatsMaxChunks ? g : kStatsMaxChunks;
-}
-
 // Strided view of a bf16 tensor [B, H, N, d] (element strides; channel stride 1).
 struct TensorArg {
   const uint16_t* ptr;
@@ -64,9 +56,6 @@ hipError_t launch_kv_quant(const TensorArg& k, const TensorArg& v, int mode, con
 // fuse_q (modes 1 and 2): quantize Q from the bf16 tensor q inside the kernel instead of reading qa's Q codes.
 hipError_t launch_attn(int mode, const TensorArg& q, const TensorArg& k, const QuantArg& qa, uint16_t* o, int64_t osb,
                        int64_t osh, int64_t osn, float sm_scale, const uint8_t* mask, bool fuse_q, hipStream_t s);
-// part: B*H*error_stats_chunks(N)*4 doubles of workspace for the per-chunk partial sums.
-hipError_t launch_error_stats(const TensorArg& a, const TensorArg& r, int B, int H, int N, int d, double* part,
-                              double* out, hipStream_t s);
 hipError_t launch_debug_qk(const QuantArg& qa, int b, int h, int q0, int nq, int k0, int nk, int32_t* out,
                            hipStream_t s);
 

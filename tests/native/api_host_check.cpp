@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "../../quantized_attention_05_amd/csrc/linear_internal.h"
+#include "../../quantized_attention_05_amd/csrc/probe_internal.h"
 #include "../../quantized_attention_05_amd/csrc/sattn_internal.h"
 
 namespace {
