@@ -300,17 +300,14 @@ __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
   __shared__ float qred[FUSEQ ? W : 1];
   uint4 qraw[FUSEQ ? 2 * KS : 1];
   if constexpr (FUSEQ) {
-    const int row = q0 + n;
-    if (row < a.qa.Nq) {
-      const uint16_t* src = a.q.ptr + b * a.q.sb + h * a.q.sh + (int64_t)row * a.q.sn + 16 * g;
+    // a row past the sequence loads the last row instead (always in bounds; no branch around the loads) and is left
+    // out of the amax and the codes
+    const int row = min(q0 + n, a.qa.Nq - 1);
+    const uint16_t* src = a.q.ptr + b * a.q.sb + h * a.q.sh + (int64_t)row * a.q.sn + 16 * g;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        qraw[2 * s] = *reinterpret_cast<const uint4*>(src + 32 * s);
-        qraw[2 * s + 1] = *reinterpret_cast<const uint4*>(src + 32 * s + 8);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 2 * KS; ++j) qraw[j] = make_uint4(0, 0, 0, 0);
+    for (int s = 0; s < KS; ++s) {
+      qraw[2 * s] = *reinterpret_cast<const uint4*>(src + 32 * s);
+      qraw[2 * s + 1] = *reinterpret_cast<const uint4*>(src + 32 * s + 8);
     }
   }
   const float* kscale = (MODE == 0) ? nullptr : a.qa.k_scales + bh * nkb;
@@ -529,21 +526,31 @@ __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
     }
   };
 
-  // ---- prologue: stages 0 .. DIST-1 as iterations 0 .. DIST-1 expect them (V of "tile -1" is zeros, read with
-  // P = 0), and K of the first tile with its scale in stage DIST for the first scores
+  // ---- prologue.  The V half of stage 0 ("tile -1", read with P = 0 by the first iteration) is zeroed before any
+  // tile load is in flight: an LDS store issued while a direct-to-LDS load is pending would wait for all of them.
+  // Then K of the first tile and its scale go to stage DIST, first, so that the first scores wait for them alone,
+  // and then stages 0 .. DIST-1 as iterations 0 .. DIST-1 expect them.
+  static_assert(G::VBYTES % (16 * RG::THREADS) == 0, "the V tile splits into whole 16-byte stores per thread");
+#pragma unroll
+  for (int j = 0; j < G::VBYTES / (16 * RG::THREADS); ++j)
+    *reinterpret_cast<uint4*>(smem + G::KBYTES + 16 * (j * RG::THREADS + (int)threadIdx.x)) = make_uint4(0, 0, 0, 0);
+  issue_k(tile_of(0), smem + DIST * G::STAGE);
+  issue_s(tile_of(0), slots + DIST * RG::SLOT);
 #pragma unroll
   for (int j = 0; j < DIST; ++j) {
     issue_k(tile_of(min(j + 1, ntile - 1)), smem + j * G::STAGE);
     if (j > 0) issue_v(tile_of(min(j - 1, ntile - 1)), smem + j * G::STAGE);
     issue_s(tile_of(min(j + 1, ntile - 1)), slots + j * RG::SLOT);
   }
-  issue_k(tile_of(0), smem + DIST * G::STAGE);
-  issue_s(tile_of(0), slots + DIST * RG::SLOT);
-  for (int i = threadIdx.x; i < G::VBYTES / 16; i += RG::THREADS)
-    *reinterpret_cast<uint4*>(smem + G::KBYTES + 16 * i) = make_uint4(0, 0, 0, 0);
+  // loads of this wave issued after the first K tile and its scale: stage 0 (K and scale), stages 1 .. DIST-1
+  constexpr int kAfterFirst = RG::KIPW + (MODE != 0) + (DIST - 1) * RG::OPS;
+  static_assert(kAfterFirst < 64, "the wait count fits vmcnt");
   PTile<MODE> pa = {}, pb = {};
   SAcc sa[2], sb[2];
   if constexpr (FUSEQ) {  // the wave's part of the Q block's amax
+    // (nothing moves above this point: the use of the Q values, and the wait for them, stays after the tile loads
+    // above are issued)
+    __builtin_amdgcn_sched_barrier(0);
     float am = 0.0f;
 #pragma unroll
     for (int j = 0; j < 2 * KS; ++j) {
@@ -552,12 +559,15 @@ __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(f[i]));
     }
+    if (q0 + n >= a.qa.Nq) am = 0.0f;  // (a row past the sequence holds a copy of the last row)
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
     if (lane == 0) qred[wave] = am;  // read after the barrier below
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  // this wave's loads up to the first K tile and its scale (and the Q rows before them) have landed; after the
+  // barrier, every wave's have
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kAfterFirst) : "memory");
+  ring_barrier();
   if constexpr (FUSEQ) {
     // the block's amax: all W waves (blk_q = 128) or this wave's pair (blk_q = 64, two blocks per workgroup)
     float am;
@@ -581,10 +591,8 @@ __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
         unpack8(qraw[2 * s + j], f);
         uint32_t lo = 0, hi = 0;
         if (row_ok) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) lo |= (uint32_t)(uint8_t)code_i8(f[i], inv) << (8 * i);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) hi |= (uint32_t)(uint8_t)code_i8(f[4 + i], inv) << (8 * i);
+          lo = codes4(f, inv);
+          hi = codes4(f + 4, inv);
         }
         wv[2 * j] = (int)lo;
         wv[2 * j + 1] = (int)hi;

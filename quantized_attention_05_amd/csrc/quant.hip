@@ -65,10 +65,8 @@ __global__ void __launch_bounds__(256) quant_q_kernel(TensorArg q, QuantArg qa) 
     const int r = rr + p * RPP;
     uint32_t lo = 0, hi = 0;
     if (!zero && r < rows) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lo |= (uint32_t)(uint8_t)code_i8(x[p][i], inv) << (8 * i);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) hi |= (uint32_t)(uint8_t)code_i8(x[p][4 + i], inv) << (8 * i);
+      lo = codes4(x[p], inv);
+      hi = codes4(x[p] + 4, inv);
     }
     *reinterpret_cast<uint2*>(dst + (int64_t)r * D + c0) = make_uint2(lo, hi);
   }
@@ -223,10 +221,8 @@ __global__ void __launch_bounds__(256) kv_quant_kernel(TensorArg k, TensorArg v,
       const int r = rr + p * RPP;
       uint32_t lo = 0, hi = 0;
       if (!zero && r < rows) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) lo |= (uint32_t)(uint8_t)code_i8(x[p][i], inv) << (8 * i);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) hi |= (uint32_t)(uint8_t)code_i8(x[p][4 + i], inv) << (8 * i);
+        lo = codes4(x[p], inv);
+        hi = codes4(x[p] + 4, inv);
       }
       *reinterpret_cast<uint2*>(dst + (int64_t)r * D + c0) = make_uint2(lo, hi);
     }

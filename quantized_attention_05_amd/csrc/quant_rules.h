@@ -18,11 +18,21 @@ __device__ __forceinline__ void unpack8(const uint4& u, float* f) {
   f[6] = bf2f(u.w & 0xFFFFu); f[7] = bf2f(u.w >> 16);
 }
 
-// code = clamp(rint(x * (127 / amax)), -127, 127), with inv = 127 / amax computed once per block
-__device__ __forceinline__ int8_t code_i8(float x, float inv) {
-  float q = rintf(x * inv);
-  q = fminf(fmaxf(q, -127.0f), 127.0f);
-  return (int8_t)(int)q;
+// The codes of four values of one block, packed into a word (the first value in the lowest byte):
+// code = clamp(rint(x * inv), -127, 127) with inv = 127 / amax computed once per block (0 for an all-zero block).
+// The clamp never acts: |x| <= amax and inv = fl(127 / amax) keep fl(x * inv) within 127 (1 + 2^-24)^2 < 127.5.
+// Adding 1.5 * 2^23 to fl(x * inv) rounds it to an integer, ties to even (the sum's spacing is 1 and 1.5 * 2^23 is
+// even), and leaves that integer in two's complement in the low byte of the sum's bits.  The multiply and the add
+// round separately (no fused multiply-add), as rint(fl(x * inv)) does.
+__device__ __forceinline__ uint32_t codes4(const float* x, float inv) {
+#pragma clang fp contract(off)
+  uint32_t b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float y = x[i] * inv;
+    b[i] = __float_as_uint(y + 12582912.0f);
+  }
+  return (b[0] & 0xFFu) | ((b[1] & 0xFFu) << 8) | ((b[2] & 0xFFu) << 16) | (b[3] << 24);
 }
 
 }  // namespace sattn
