@@ -43,3 +43,35 @@ def test_traffic_is_null_for_another_kernel_source_or_workload(monkeypatch):
     assert bench.measured_traffic("tiny", 2, 1.0) is None              # no counter record for that workload
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)  # the kernel changed after the counters
     assert bench.measured_traffic("wan14b-720p", 2, 1.0) is None
+
+
+def test_record_traffic_reads_counter_runs(tmp_path, monkeypatch):
+    """--record-traffic turns four rocprofv3 counter tables (kernel and copy, FETCH_SIZE and WRITE_SIZE) into the
+    traffic record: counter values summed per dispatch over their instances, scaled by the copy's calibration."""
+    kernel = "void sattn::(anonymous namespace)::attn_pipe_kernel<2, 128, 4, false, false>(sattn::AttnArg)"
+    fused = "void sattn::(anonymous namespace)::attn_pipe_kernel<2, 128, 4, false, true>(sattn::AttnArg)"
+    header = "Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n"
+
+    def table(run, rows):
+        d = tmp_path / run
+        d.mkdir()
+        (d / "run_counter_collection.csv").write_text(
+            header + "".join(f'{i},"{n}",C,{v}\n' for i, n, v in rows))
+
+    # two dispatches of the timed kernel, each counted in two instances; one of the fused kernel (ignored)
+    table("pmc_FETCH_SIZE", [(1, fused, 9e9), (2, kernel, 100.0), (2, kernel, 300.0), (3, kernel, 500.0),
+                             (3, kernel, 100.0)])
+    table("pmc_WRITE_SIZE", [(2, kernel, 40.0), (3, kernel, 60.0)])
+    table("copy_FETCH_SIZE", [(1, "fill", 5.0), (2, "__amd_rocclr_copyBuffer", 131072.0)])
+    table("copy_WRITE_SIZE", [(2, "__amd_rocclr_copyBuffer", 262144.0)])
+    out = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
+    bench.record_traffic(str(tmp_path), "wan14b-720p", 2)
+    rec = json.loads(out.read_text())["wan14b-720p/mode2"]
+    assert rec["fetch_kib_per_dispatch"] == [400.0, 600.0] and rec["write_kib_per_dispatch"] == [40.0, 60.0]
+    assert rec["copy_calibration"]["fetch_factor"] == 2.0 and rec["copy_calibration"]["write_factor"] == 1.0
+    assert rec["fetch_bytes"] == 500 * 2 * 1024 and rec["write_bytes"] == 50 * 1024
+    assert rec["kernel_source_sha"] == bench.kernel_source_hash()
+    # the record it wrote is the one the benchmark then reports
+    got = bench.measured_traffic("wan14b-720p", 2, 1.0)
+    assert got["total_bytes"] == rec["fetch_bytes"] + rec["write_bytes"]
