@@ -15,18 +15,21 @@ from parity_helpers import device_inputs, head_bits, say, u16
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("d,layout,n", [(128, "bhnd", 300), (64, "bhnd", 300), (128, "bnhd", 300),
-                                        (128, "bhnd", 16500), (64, "bnhd", 16500), (128, "bhnd", 255)])
-def test_error_stats_match_the_definition(d, layout, n):
+@pytest.mark.parametrize("d,layout,n,batch", [(128, "bhnd", 300, 1), (64, "bhnd", 300, 1), (128, "bnhd", 300, 1),
+                                              (128, "bhnd", 16500, 1), (64, "bnhd", 16500, 1), (128, "bhnd", 255, 1),
+                                              (128, "bnhd", 700, 2)])
+def test_error_stats_match_the_definition(d, layout, n, batch):
     """N = 300 sums each head in 2 row chunks, N = 16500 in 64 chunks of 258 rows with a ragged last one (246),
-    N = 255 in a single chunk shorter than the workgroup's stride."""
-    w = wl.scaled(wl.WORKLOADS["wan14b-720p"], name="probe-stats", H=3, Nq=n, Nkv=n, d=d, seed=61)
+    N = 255 in a single chunk shorter than the workgroup's stride; B = 2 puts the (batch, head) pairs in the grid's
+    second dimension."""
+    w = wl.scaled(wl.WORKLOADS["wan14b-720p"], name="probe-stats", B=batch, H=3, Nq=n, Nkv=n, d=d, seed=61)
     q, k, v = device_inputs(w, layout=layout)
     stats = sattn.error_stats(q, k).cpu().numpy()  # any two bf16 tensors of one shape
     qh, kh = u16(q), u16(k)
-    for h in range(w.H):
-        ref = oracle.error_stats(qh[0, h], kh[0, h])
-        assert np.allclose(stats[0, h], ref, rtol=1e-12, atol=0), (h, stats[0, h], ref)
+    for b in range(w.B):
+        for h in range(w.H):
+            ref = oracle.error_stats(qh[b, h], kh[b, h])
+            assert np.allclose(stats[b, h], ref, rtol=1e-12, atol=0), (b, h, stats[b, h], ref)
     same = sattn.error_stats(q, q).cpu().numpy()
     assert np.all(same[..., 0] == 0) and np.all(same[..., 1] == same[..., 2]) and np.all(same[..., 2] == same[..., 3])
     # deterministic, and independent of what the workspace held before the call
