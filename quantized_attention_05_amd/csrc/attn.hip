@@ -526,106 +526,166 @@ __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
     }
   };
 
-  // ---- prologue.  The V half of stage 0 ("tile -1", read with P = 0 by the first iteration) is zeroed before any
-  // tile load is in flight: an LDS store issued while a direct-to-LDS load is pending would wait for all of them.
-  // Then K of the first tile and its scale go to stage DIST, first, so that the first scores wait for them alone,
-  // and then stages 0 .. DIST-1 as iterations 0 .. DIST-1 expect them.
-  static_assert(G::VBYTES % (16 * RG::THREADS) == 0, "the V tile splits into whole 16-byte stores per thread");
+  if constexpr (MODE == 0 && D == 128 && !SPARSE) {
+    // ---- dense bf16 at d = 128: one tile per iteration, without the software pipeline.  Stage i % R holds K and V
+    // of tile i; iteration i loads tile i + DIST into stage (i + DIST) % R, whose last reader was iteration i - 1.
+    // At this instance's register count the compiler issues a step's matrix ops ahead of its softmax whichever form
+    // the loop takes, so the pipeline's second score and P buffers (48 registers) bought nothing here.  (At d = 64
+    // and with a block-sparse mask this form takes more registers than the pipelined one.)
 #pragma unroll
-  for (int j = 0; j < G::VBYTES / (16 * RG::THREADS); ++j)
-    *reinterpret_cast<uint4*>(smem + G::KBYTES + 16 * (j * RG::THREADS + (int)threadIdx.x)) = make_uint4(0, 0, 0, 0);
-  issue_k(tile_of(0), smem + DIST * G::STAGE);
-  issue_s(tile_of(0), slots + DIST * RG::SLOT);
-#pragma unroll
-  for (int j = 0; j < DIST; ++j) {
-    issue_k(tile_of(min(j + 1, ntile - 1)), smem + j * G::STAGE);
-    if (j > 0) issue_v(tile_of(min(j - 1, ntile - 1)), smem + j * G::STAGE);
-    issue_s(tile_of(min(j + 1, ntile - 1)), slots + j * RG::SLOT);
-  }
-  // loads of this wave issued after the first K tile and its scale: stage 0 (K and scale), stages 1 .. DIST-1
-  constexpr int kAfterFirst = RG::KIPW + (MODE != 0) + (DIST - 1) * RG::OPS;
-  static_assert(kAfterFirst < 64, "the wait count fits vmcnt");
-  PTile<MODE> pa = {}, pb = {};
-  SAcc sa[2], sb[2];
-  if constexpr (FUSEQ) {  // the wave's part of the Q block's amax
-    // (nothing moves above this point: the use of the Q values, and the wait for them, stays after the tile loads
-    // above are issued)
-    __builtin_amdgcn_sched_barrier(0);
-    float am = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 2 * KS; ++j) {
-      float f[8];
-      unpack8(qraw[j], f);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(f[i]));
+    for (int j = 0; j < DIST; ++j) {
+      issue_k(tile_of(min(j, ntile - 1)), smem + j * G::STAGE);
+      issue_v(tile_of(min(j, ntile - 1)), smem + j * G::STAGE);
     }
-    if (q0 + n >= a.qa.Nq) am = 0.0f;  // (a row past the sequence holds a copy of the last row)
+    // iteration `it` from stage SRD (TAIL: the sequence's ragged last tile)
+    auto one = [&](int it, auto slot_tag, auto tail_tag) __attribute__((always_inline)) {
+      constexpr int SRD = decltype(slot_tag)::value;
+      constexpr int SWR = (SRD + DIST) % R;
+      wait_loads();
+      ring_barrier();  // stage SRD is visible to every wave; every wave is done with stage SWR
+      // past the end these reload the last tile, which nothing reads again
+      issue_k(tile_of(min(it + DIST, ntile - 1)), smem + SWR * G::STAGE);
+      issue_v(tile_of(min(it + DIST, ntile - 1)), smem + SWR * G::STAGE);
+      const uint8_t* rd = smem + SRD * G::STAGE;
+      SAcc sc[2];
+      qk(rd, sc);
+      PTile<MODE> pc;
+      const float mold = m;
+      const float alpha = softmax(sc, fq, Nkv - tile_of(it) * kTile, pc, tail_tag);
+      if (it > 0 && __any(m != mold)) {  // (on the first tile the accumulator is still zero)
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
-    if (lane == 0) qred[wave] = am;  // read after the barrier below
-  }
-  // this wave's loads up to the first K tile and its scale (and the Q rows before them) have landed; after the
-  // barrier, every wave's have
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kAfterFirst) : "memory");
-  ring_barrier();
-  if constexpr (FUSEQ) {
-    // the block's amax: all W waves (blk_q = 128) or this wave's pair (blk_q = 64, two blocks per workgroup)
-    float am;
-    if (a.qa.blk_q == 128) {
-      am = qred[0];
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int w = 1; w < W; ++w) am = fmaxf(am, qred[w]);
-    } else {
-      am = fmaxf(qred[wave & ~1], qred[wave | 1]);
-    }
-    const bool zero = !(am >= kGuard);
-    const float inv = zero ? 0.0f : 127.0f / am;
-    fq = (zero ? 0.0f : am / 127.0f) * a.clog2e;
-    const bool row_ok = !zero && q0 + n < a.qa.Nq;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      int wv[4];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        float f[8];
-        unpack8(qraw[2 * s + j], f);
-        uint32_t lo = 0, hi = 0;
-        if (row_ok) {
-          lo = codes4(f, inv);
-          hi = codes4(f + 4, inv);
-        }
-        wv[2 * j] = (int)lo;
-        wv[2 * j + 1] = (int)hi;
+          for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
       }
-      qf8[s] = (v4i){wv[0], wv[1], wv[2], wv[3]};
+      pv(rd, pc);
+    };
+    auto at_slot = [&](int it, auto tail_tag) __attribute__((always_inline)) {
+      static_assert(R <= 4, "stage offsets are compile-time for up to four stages");
+      const int sl = it % R;
+      if (sl == 0) one(it, std::integral_constant<int, 0>{}, tail_tag);
+      else if (sl == 1) one(it, std::integral_constant<int, 1 % R>{}, tail_tag);
+      else if (sl == 2) one(it, std::integral_constant<int, 2 % R>{}, tail_tag);
+      else one(it, std::integral_constant<int, 3 % R>{}, tail_tag);
+    };
+    // groups of R iterations with constant stage offsets, the rest one by one; only the sequence's last tile can be
+    // ragged
+    const int nlast = ntile - 1;
+    int it = 0;
+    static_assert(R == 2 || R == 4, "two or four stages");
+    for (; it + R <= nlast; it += R) {
+      one(it, std::integral_constant<int, 0>{}, std::false_type{});
+      one(it + 1, std::integral_constant<int, 1>{}, std::false_type{});
+      if constexpr (R == 4) {
+        one(it + 2, std::integral_constant<int, 2 % R>{}, std::false_type{});
+        one(it + 3, std::integral_constant<int, 3 % R>{}, std::false_type{});
+      }
     }
-  }
-  ks = (MODE == 0) ? 1.0f : *reinterpret_cast<const float*>(slots + DIST * RG::SLOT);
-  qk(smem + DIST * G::STAGE, sa);
+    for (; it < nlast; ++it) at_slot(it, std::false_type{});
+    if (Nkv % kTile && tile_of(it) == nkb - 1) at_slot(it, std::true_type{});
+    else at_slot(it, std::false_type{});
+  } else {
+    // ---- prologue.  The V half of stage 0 ("tile -1", read with P = 0 by the first iteration) is zeroed before any
+    // tile load is in flight: an LDS store issued while a direct-to-LDS load is pending would wait for all of them.
+    // Then K of the first tile and its scale go to stage DIST, first, so that the first scores wait for them alone,
+    // and then stages 0 .. DIST-1 as iterations 0 .. DIST-1 expect them.
+    static_assert(G::VBYTES % (16 * RG::THREADS) == 0, "the V tile splits into whole 16-byte stores per thread");
+  #pragma unroll
+    for (int j = 0; j < G::VBYTES / (16 * RG::THREADS); ++j)
+      *reinterpret_cast<uint4*>(smem + G::KBYTES + 16 * (j * RG::THREADS + (int)threadIdx.x)) = make_uint4(0, 0, 0, 0);
+    issue_k(tile_of(0), smem + DIST * G::STAGE);
+    issue_s(tile_of(0), slots + DIST * RG::SLOT);
+  #pragma unroll
+    for (int j = 0; j < DIST; ++j) {
+      issue_k(tile_of(min(j + 1, ntile - 1)), smem + j * G::STAGE);
+      if (j > 0) issue_v(tile_of(min(j - 1, ntile - 1)), smem + j * G::STAGE);
+      issue_s(tile_of(min(j + 1, ntile - 1)), slots + j * RG::SLOT);
+    }
+    // loads of this wave issued after the first K tile and its scale: stage 0 (K and scale), stages 1 .. DIST-1
+    constexpr int kAfterFirst = RG::KIPW + (MODE != 0) + (DIST - 1) * RG::OPS;
+    static_assert(kAfterFirst < 64, "the wait count fits vmcnt");
+    PTile<MODE> pa = {}, pb = {};
+    SAcc sa[2], sb[2];
+    if constexpr (FUSEQ) {  // the wave's part of the Q block's amax
+      // (nothing moves above this point: the use of the Q values, and the wait for them, stays after the tile loads
+      // above are issued)
+      __builtin_amdgcn_sched_barrier(0);
+      float am = 0.0f;
+  #pragma unroll
+      for (int j = 0; j < 2 * KS; ++j) {
+        float f[8];
+        unpack8(qraw[j], f);
+  #pragma unroll
+        for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(f[i]));
+      }
+      if (q0 + n >= a.qa.Nq) am = 0.0f;  // (a row past the sequence holds a copy of the last row)
+  #pragma unroll
+      for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
+      if (lane == 0) qred[wave] = am;  // read after the barrier below
+    }
+    // this wave's loads up to the first K tile and its scale (and the Q rows before them) have landed; after the
+    // barrier, every wave's have
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kAfterFirst) : "memory");
+    ring_barrier();
+    if constexpr (FUSEQ) {
+      // the block's amax: all W waves (blk_q = 128) or this wave's pair (blk_q = 64, two blocks per workgroup)
+      float am;
+      if (a.qa.blk_q == 128) {
+        am = qred[0];
+  #pragma unroll
+        for (int w = 1; w < W; ++w) am = fmaxf(am, qred[w]);
+      } else {
+        am = fmaxf(qred[wave & ~1], qred[wave | 1]);
+      }
+      const bool zero = !(am >= kGuard);
+      const float inv = zero ? 0.0f : 127.0f / am;
+      fq = (zero ? 0.0f : am / 127.0f) * a.clog2e;
+      const bool row_ok = !zero && q0 + n < a.qa.Nq;
+  #pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        int wv[4];
+  #pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          float f[8];
+          unpack8(qraw[2 * s + j], f);
+          uint32_t lo = 0, hi = 0;
+          if (row_ok) {
+            lo = codes4(f, inv);
+            hi = codes4(f + 4, inv);
+          }
+          wv[2 * j] = (int)lo;
+          wv[2 * j + 1] = (int)hi;
+        }
+        qf8[s] = (v4i){wv[0], wv[1], wv[2], wv[3]};
+      }
+    }
+    ks = (MODE == 0) ? 1.0f : *reinterpret_cast<const float*>(slots + DIST * RG::SLOT);
+    qk(smem + DIST * G::STAGE, sa);
 
-  // ---- iterations 0 .. ntile-2 have a next tile; groups of R run with constant stage offsets
-  const int nmain = ntile - 1;
-  int i = 0;
-  for (; i + R <= nmain; i += R) {
-    step(i, 0, sa, sb, pa, pb, std::false_type{}, std::true_type{});
-    step(i + 1, 1, sb, sa, pb, pa, std::false_type{}, std::true_type{});
-    if constexpr (R == 4) {
-      step(i + 2, 2, sa, sb, pa, pb, std::false_type{}, std::true_type{});
-      step(i + 3, 3, sb, sa, pb, pa, std::false_type{}, std::true_type{});
+    // ---- iterations 0 .. ntile-2 have a next tile; groups of R run with constant stage offsets
+    const int nmain = ntile - 1;
+    int i = 0;
+    for (; i + R <= nmain; i += R) {
+      step(i, 0, sa, sb, pa, pb, std::false_type{}, std::true_type{});
+      step(i + 1, 1, sb, sa, pb, pa, std::false_type{}, std::true_type{});
+      if constexpr (R == 4) {
+        step(i + 2, 2, sa, sb, pa, pb, std::false_type{}, std::true_type{});
+        step(i + 3, 3, sb, sa, pb, pa, std::false_type{}, std::true_type{});
+      }
     }
+    for (; i < nmain; ++i) {
+      step(i, i % R, sa, sb, pa, pb, std::false_type{}, std::true_type{});
+      sa[0] = sb[0];
+      sa[1] = sb[1];
+      pa = pb;
+    }
+    // i = ntile - 1: the last tile; only the sequence's last tile can be ragged
+    if (Nkv % kTile && tile_of(i) == nkb - 1) step(i, i % R, sa, sb, pa, pb, std::true_type{}, std::false_type{});
+    else step(i, i % R, sa, sb, pa, pb, std::false_type{}, std::false_type{});
+    wait_loads();
+    ring_barrier();
+    pv(smem + (ntile % R) * G::STAGE, pb);
   }
-  for (; i < nmain; ++i) {
-    step(i, i % R, sa, sb, pa, pb, std::false_type{}, std::true_type{});
-    sa[0] = sb[0];
-    sa[1] = sb[1];
-    pa = pb;
-  }
-  // i = ntile - 1: the last tile; only the sequence's last tile can be ragged
-  if (Nkv % kTile && tile_of(i) == nkb - 1) step(i, i % R, sa, sb, pa, pb, std::true_type{}, std::false_type{});
-  else step(i, i % R, sa, sb, pa, pb, std::false_type{}, std::false_type{});
-  wait_loads();
-  ring_barrier();
-  pv(smem + (ntile % R) * G::STAGE, pb);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no tile load may still be writing LDS when the wave exits
 
   // ---------------- epilogue: O = acc / l  (mode 2: acc * s_v[c] / (448 l)), bf16, lane writes D/2 channels
