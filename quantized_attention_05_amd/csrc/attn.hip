@@ -336,13 +336,22 @@ __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
     if constexpr (MODE == 0) {
       acc[0] = (v16f){};
       acc[1] = (v16f){};
+      // the operands of two k-steps are read before their four matrix ops, so that reads stay in flight while the
+      // matrix cores run (read by read, every op waited for its own operand; four k-steps at once spill)
+      constexpr int GRP = 2;
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
+      for (int s0 = 0; s0 < KS; s0 += GRP) {
+        v8bf kv[GRP][2];
 #pragma unroll
-        for (int bm = 0; bm < 2; ++bm) {
-          const v8bf kv = *reinterpret_cast<const v8bf*>(st + k_rd[bm][s]);
-          acc[bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qfb[s], acc[bm], 0, 0, 0);
-        }
+        for (int s = 0; s < GRP; ++s)
+#pragma unroll
+          for (int bm = 0; bm < 2; ++bm) kv[s][bm] = *reinterpret_cast<const v8bf*>(st + k_rd[bm][s0 + s]);
+#pragma unroll
+        for (int s = 0; s < GRP; ++s)
+#pragma unroll
+          for (int bm = 0; bm < 2; ++bm)
+            acc[bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[s][bm], qfb[s0 + s], acc[bm], 0, 0, 0);
+      }
     } else {
       acc[0] = bias_acc;
       acc[1] = bias_acc;
@@ -363,6 +372,16 @@ __global__ void __launch_bounds__(64 * W, 8 / W) attn_pipe_kernel(AttnArg a) {
         const v4i hi = *reinterpret_cast<const v4i*>(st + v_rd[cb][1]);
         const v8i vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         oacc[cb] = mfma_e4m3(vv, p.w, oacc[cb]);
+      }
+    } else if constexpr (MODE == 0) {
+      // (bf16 scores: the four V reads of a channel block go out before its four matrix ops, as in the scores above)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        v8bf vv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vv[j] = *reinterpret_cast<const v8bf*>(st + v_rd[cb][j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv[j], p.b[j], oacc[cb], 0, 0, 0);
       }
     } else {
 #pragma unroll
