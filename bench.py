@@ -270,7 +270,8 @@ def layer_probe(args):
 def linear_layers(args):
     """The quantized linear layer at the Wan-14B 720p shapes (75 600 tokens): one JSON line per shape with W8A8 (the
     headline: effective TOPS over 2 M N K), W8A16, the GEMM kernel alone on prepared codes, the activation
-    quantization alone, and torch's bf16 linear (hipBLASLt) on the same tensors as context."""
+    quantization alone, and, as context, torch's bf16 linear and its plain INT8 matrix product (`torch._int_mm`:
+    int32 out, no block scales, no bias; both hipBLASLt) on the same tensors and codes."""
     import torch
 
     from quantized_attention_05_amd import sattn
@@ -305,6 +306,8 @@ def linear_layers(args):
         gemm8 = timed(lambda: sattn.linear_quantized(xq, sx, wq, sw, b, out=y), args.steps)
         quant = timed(lambda: sattn.quantize_blocks(x), args.steps)
         bf16 = timed(lambda: torch.nn.functional.linear(x, wt, b), args.steps)
+        # the vendor library's plain INT8 GEMM on the same codes (int32 out, no block scales, no bias)
+        int8mm = timed(lambda: torch._int_mm(xq, wq.t()), args.steps)
         tops = lambda ms: round(w.ops / (ms * 1e-3) / 1e12, 1)
         print(json.dumps({
             "metric": f"quantized linear layer TOPS (2 M N K), Wan-14B 720p {name.split('720p-')[1]}",
@@ -319,6 +322,7 @@ def linear_layers(args):
             "quantize_x_ms": round(quant, 4),
             "quantize_x_gbps": round(w.M * w.K * 3 / (quant * 1e-3) / 1e9, 1),
             "torch_bf16_linear_ms": round(bf16, 4), "torch_bf16_linear_tops": tops(bf16),
+            "torch_int8_mm_ms": round(int8mm, 4), "torch_int8_mm_tops": tops(int8mm),
         }), flush=True)
         del x, wt, b, wq, sw, y, ws, xq, sx
         torch.cuda.empty_cache()
