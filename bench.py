@@ -141,11 +141,13 @@ def layer_selective(args):
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sampler = GpuSampler().start()
     e0.record(stream)
     for _ in range(args.steps):
         one_pass()
     e1.record(stream)
     torch.cuda.synchronize()
+    gpu_state = sampler.stop()
     ms = e0.elapsed_time(e1) / args.steps
     ops = wl.LAYERSEL_LAYERS * (ws_.ops + wc_.ops)
     print(json.dumps({
@@ -158,6 +160,7 @@ def layer_selective(args):
                    "modes": "".join(str(m) for m in modes), "self": [ws_.H, ws_.Nq, ws_.d],
                    "cross_nkv": wc_.Nkv, "cross_mode": "bf16"},
         "pct_int8_mfma_peak": round(100.0 * ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2),
+        "gpu_clock_power": gpu_state,
     }), flush=True)
 
 
@@ -382,6 +385,70 @@ def cpu_baseline(w, mode: int, budget_s: float):
     }
 
 
+class GpuSampler:
+    """Samples the GPU's power draw and its current core clock from sysfs (hwmon `power1_input`, `power1_cap`; the
+    current level of `pp_dpm_sclk`) on a host thread while the timed steps run; reads files only, no GPU calls.
+    Reports None where the files are missing (not an AMD GPU driver, or no permission)."""
+
+    def __init__(self, period_s: float = 0.01):
+        import glob
+        import threading
+
+        self.period_s, self.samples, self._stop = period_s, [], threading.Event()
+        self.dev = None
+        for d in sorted(glob.glob("/sys/class/drm/card*/device")):
+            try:
+                if open(f"{d}/vendor").read().strip() == "0x1002" and glob.glob(f"{d}/hwmon/hwmon*/power1_input"):
+                    self.dev = d
+                    break
+            except OSError:
+                continue
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        import glob
+
+        hw = glob.glob(f"{self.dev}/hwmon/hwmon*")[0]
+        power = int(open(f"{hw}/power1_input").read()) / 1e6
+        mhz = None
+        for line in open(f"{self.dev}/pp_dpm_sclk"):
+            if line.rstrip().endswith("*"):
+                mhz = int(line.split(":")[1].strip().split("M")[0])
+        return power, mhz
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except (OSError, ValueError, IndexError):
+                return
+            self._stop.wait(self.period_s)
+
+    def start(self):
+        if self.dev:
+            self._thread.start()
+        return self
+
+    def stop(self):
+        if not self.dev:
+            return None
+        self._stop.set()
+        self._thread.join()
+        try:
+            hw = __import__("glob").glob(f"{self.dev}/hwmon/hwmon*")[0]
+            cap = int(open(f"{hw}/power1_cap").read()) / 1e6
+        except (OSError, ValueError, IndexError):
+            cap = None
+        pw = sorted(p for p, _ in self.samples)
+        mhz = sorted(c for _, c in self.samples if c is not None)
+        med = lambda xs: xs[len(xs) // 2] if xs else None
+        return {"power_cap_w": cap, "power_w_median": med(pw), "power_w_max": pw[-1] if pw else None,
+                "sclk_mhz_median": med(mhz), "sclk_mhz_min": mhz[0] if mhz else None,
+                "sclk_mhz_max": mhz[-1] if mhz else None, "samples": len(self.samples),
+                "source": f"{self.dev}: hwmon power1_input / power1_cap, current pp_dpm_sclk level, "
+                          f"every {self.period_s * 1e3:.0f} ms during the timed steps"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -469,6 +536,7 @@ def main():
     # one event between consecutive steps as well, for the per-step spread (median, min, max)
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
+    sampler = GpuSampler().start()
     wall0 = time.perf_counter()
     e0.record(stream)
     marks[0].record(stream)
@@ -478,6 +546,7 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    gpu_state = sampler.stop()
     ms_per_step = e0.elapsed_time(e1) / args.steps
     value = w.ops / (ms_per_step * 1e-3) / 1e12
     step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
@@ -550,6 +619,7 @@ def main():
             "ops_per_launch": w.ops,
         },
         "wall_s_timed_region": round(wall, 3),
+        "gpu_clock_power": gpu_state,
         "input_generation_s": round(gen_s, 1),
     }
     if not args.no_cpu_baseline:

@@ -75,3 +75,27 @@ def test_record_traffic_reads_counter_runs(tmp_path, monkeypatch):
     # the record it wrote is the one the benchmark then reports
     got = bench.measured_traffic("wan14b-720p", 2, 1.0)
     assert got["total_bytes"] == rec["fetch_bytes"] + rec["write_bytes"]
+
+
+def test_gpu_sampler_reads_sysfs_files_only(tmp_path, monkeypatch):
+    """The clock/power sampler reads hwmon power and the current pp_dpm_sclk level from sysfs, and reports None when
+    there is no AMD card to read (as in a container without a GPU)."""
+    card = tmp_path / "card0" / "device"
+    (card / "hwmon" / "hwmon3").mkdir(parents=True)
+    (card / "vendor").write_text("0x1002\n")
+    (card / "hwmon" / "hwmon3" / "power1_input").write_text("1288000000\n")
+    (card / "hwmon" / "hwmon3" / "power1_cap").write_text("1400000000\n")
+    (card / "pp_dpm_sclk").write_text("S: 1973Mhz *\n0: 500Mhz\n1: 2400Mhz\n")
+    import glob as globmod
+
+    real_glob = globmod.glob
+    monkeypatch.setattr(globmod, "glob", lambda p: real_glob(p.replace("/sys/class/drm", str(tmp_path))))
+    s = bench.GpuSampler(period_s=0.001).start()
+    import time
+
+    time.sleep(0.02)
+    out = s.stop()
+    assert out["power_cap_w"] == 1400.0 and out["power_w_median"] == 1288.0
+    assert out["sclk_mhz_median"] == 1973 and out["samples"] >= 1
+    monkeypatch.setattr(globmod, "glob", lambda p: [])
+    assert bench.GpuSampler().start().stop() is None
