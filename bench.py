@@ -141,7 +141,7 @@ def layer_selective(args):
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    sampler = GpuSampler().start()
+    sampler = GpuSampler(pci=gpu_pci_address()).start()
     e0.record(stream)
     for _ in range(args.steps):
         one_pass()
@@ -385,24 +385,39 @@ def cpu_baseline(w, mode: int, budget_s: float):
     }
 
 
+def gpu_pci_address(index: int = 0) -> str | None:
+    """The PCI address of torch's GPU `index` as sysfs names it ("0000:75:00.0"), or None if torch does not say."""
+    import torch
+
+    p = torch.cuda.get_device_properties(index)
+    try:
+        return f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
+    except AttributeError:
+        return None
+
+
 class GpuSampler:
     """Samples the GPU's power draw and its current core clock from sysfs (hwmon `power1_input`, `power1_cap`; the
     current level of `pp_dpm_sclk`) on a host thread while the timed steps run; reads files only, no GPU calls.
     Reports None where the files are missing (not an AMD GPU driver, or no permission)."""
 
-    def __init__(self, period_s: float = 0.01):
+    def __init__(self, period_s: float = 0.01, pci: str | None = None):
+        """pci: the PCI address ("0000:75:00.0") of the GPU to read."""
         import glob
+        import os
         import threading
 
         self.period_s, self.samples, self._stop = period_s, [], threading.Event()
-        self.dev = None
+        cards = []
         for d in sorted(glob.glob("/sys/class/drm/card*/device")):
             try:
                 if open(f"{d}/vendor").read().strip() == "0x1002" and glob.glob(f"{d}/hwmon/hwmon*/power1_input"):
-                    self.dev = d
-                    break
+                    cards.append(d)
             except OSError:
                 continue
+        match = [d for d in cards if pci is not None and os.path.basename(os.path.realpath(d)).lower() == pci.lower()]
+        # the card at that PCI address; else the only AMD card there is; else none (rather than another GPU's)
+        self.dev = match[0] if match else (cards[0] if len(cards) == 1 else None)
         self._thread = threading.Thread(target=self._run, daemon=True)
 
     def _read(self):
@@ -536,7 +551,7 @@ def main():
     # one event between consecutive steps as well, for the per-step spread (median, min, max)
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    sampler = GpuSampler().start()
+    sampler = GpuSampler(pci=gpu_pci_address()).start()
     wall0 = time.perf_counter()
     e0.record(stream)
     marks[0].record(stream)
