@@ -86,7 +86,10 @@ LARGE = [
     ("wan14b-720p", W["wan14b-720p"], 2),
     ("wan14b-720p", W["wan14b-720p"], 1),
     ("wan14b-720p", W["wan14b-720p"], 0),
+    ("layersel-720p-self", W["layersel-720p-self"], 2),
+    ("layersel-720p-self", W["layersel-720p-self"], 0),
     ("layersel-720p-cross", W["layersel-720p-cross"], 0),
+    ("layersel-720p-cross", W["layersel-720p-cross"], 1),
     ("layersel-720p-cross", W["layersel-720p-cross"], 2),
 ]
 
